@@ -1,0 +1,244 @@
+"""CPU oracle for the Atom W4A4 mixed-precision quantized linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no code with the
+HIP library (no kernels, headers, tables or helpers) and imports nothing from it.
+
+Plain numpy, written for a reader to check against the pages by eye.  Sources, by page
+title and section:
+
+* "Atom: Low-bit Quantization for Efficient and Accurate LLM Serving" -- index page,
+  section "Abstract (arXiv)": 4-bit weight-activation quantization built on 4-bit integer
+  operators, mixed precision plus fine-grained quantization.
+* Same title, curated summary page, method paragraph: weights grouped into small blocks
+  with per-group scales; activations get a dedicated higher-precision outlier path.
+* "Atom (mixed-precision block-outlier low-bit quantization for serving)" -- quantization
+  record, Fields "Bits" (w4a4 with outlier channels at higher precision), "Weight group
+  size" (128), "Activation scheme" (dense bulk 4-bit, a small set of outlier channels
+  kept at higher precision) and "notes" (every contiguous run of 128 elements is one
+  independently quantized group; a 128-channel high-precision group; effective bits ~4;
+  integer operators, not FP4 tensor cores).
+
+Readings taken where the pages are silent (each one is also a parameter of the HIP path):
+
+* outlier statistic: sum of squares of each input channel over the calibration tokens,
+  as the exactly rounded fp64 value; the 128 largest are outliers, ties to the lower
+  channel index; one global set per layer shared by X and W;
+* reorder: non-outlier channels ascending, then the outlier channels ascending;
+* quantizer: symmetric absmax, no zero point, no clipping; INT4 codes in [-7, 7] for the
+  bulk groups, INT8 codes in [-127, 127] for the outlier group;
+* scale: fp32 correctly rounded ``absmax / qmax``, rounded to nearest-even fp16 and stored
+  fp16, group-major ``[G, rows]``; codes ``clamp(rint_even(fl32(x / s)))``; a zero scale
+  gives zero codes;
+* packing: two's-complement nibbles, the even-indexed code in the low nibble; the 128
+  INT8 outlier codes are appended as the last 128 bytes of each row;
+* output: ``Y = sum_g acc_g * sx_g * sw_g`` rounded once to fp16 (round to nearest even).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+GROUP = 128          # quantization group: 128 contiguous elements (record, "Weight group size"; "notes")
+OUTLIERS = 128       # high-precision outlier channels (record, "notes")
+QMAX_INT4 = 7        # symmetric INT4 range for the dense bulk (record, "Bits")
+QMAX_INT8 = 127      # symmetric INT8 range for the outlier group (higher precision; record, "Bits")
+
+
+# --------------------------------------------------------------------------- shapes
+def num_groups(K: int) -> int:
+    """G = K / 128: groups 0..G-2 are INT4, group G-1 is the INT8 outlier group."""
+    if K % GROUP or K < 2 * GROUP:
+        raise ValueError(f"K={K} must be a multiple of {GROUP} and at least {2 * GROUP}")
+    return K // GROUP
+
+
+def row_bytes(K: int) -> int:
+    """Bytes of one packed row: (K-128) INT4 codes at 2 per byte, then 128 INT8 codes."""
+    num_groups(K)
+    return (K - OUTLIERS) // 2 + OUTLIERS
+
+
+# --------------------------------------------------------------------------- step: outlier selection
+def channel_stat(X: np.ndarray) -> np.ndarray:
+    """Per input channel, the sum of squares over the calibration rows.
+
+    Every fp16 square is exact in fp64, and ``math.fsum`` returns the correctly rounded
+    value of the exact sum, so the result does not depend on the summation order."""
+    X64 = np.asarray(X, dtype=np.float16).astype(np.float64)
+    sq = np.ascontiguousarray((X64 * X64).T)
+    return np.array([math.fsum(sq[c].tolist()) for c in range(sq.shape[0])], dtype=np.float64)
+
+
+def select_outliers(stat: np.ndarray, n: int = OUTLIERS) -> np.ndarray:
+    """Indices (ascending) of the ``n`` channels with the largest statistic; ties go to the
+    lower channel index."""
+    stat = np.asarray(stat, dtype=np.float64)
+    order = sorted(range(stat.shape[0]), key=lambda c: (-stat[c], c))
+    return np.array(sorted(order[:n]), dtype=np.int64)
+
+
+def make_perm(K: int, outliers: np.ndarray) -> np.ndarray:
+    """Reordered channel j takes original channel perm[j]: the non-outlier channels in
+    ascending order, then the outlier channels in ascending order (outliers at the tail)."""
+    is_out = np.zeros(K, dtype=bool)
+    is_out[np.asarray(outliers)] = True
+    if is_out.sum() != OUTLIERS:
+        raise ValueError("need exactly 128 distinct outlier channels")
+    return np.concatenate([np.nonzero(~is_out)[0], np.nonzero(is_out)[0]]).astype(np.int32)
+
+
+def outlier_perm(X_calib: np.ndarray) -> np.ndarray:
+    """Calibration rows -> perm (statistic, top-128 selection, reorder)."""
+    K = X_calib.shape[1]
+    return make_perm(K, select_outliers(channel_stat(X_calib)))
+
+
+# --------------------------------------------------------------------------- step: quantize one row set
+def quantize_rows(X: np.ndarray, perm: np.ndarray):
+    """Reorder the columns of fp16 ``X`` [rows, K] through ``perm`` and quantize each
+    128-wide group of each row independently.
+
+    Returns ``(codes int8 [rows, K], scales fp16 [G, rows])``: groups 0..G-2 hold INT4
+    codes in [-7, 7], group G-1 (the 128 outlier channels) holds INT8 codes in [-127, 127].
+    """
+    X = np.asarray(X)
+    if X.dtype != np.float16:
+        raise TypeError("X must be float16")
+    rows, K = X.shape
+    G = num_groups(K)
+    perm = np.asarray(perm, dtype=np.int64)
+    xr = X[:, perm].astype(np.float32).reshape(rows, G, GROUP)     # fp16 -> fp32 is exact
+
+    qmax = np.full(G, QMAX_INT4, dtype=np.float32)
+    qmax[G - 1] = QMAX_INT8
+    a = np.max(np.abs(xr), axis=2)                                   # group absmax (exact)
+    s32 = a / qmax[None, :]                                          # IEEE fp32 division
+    s16 = s32.astype(np.float16)                                     # round to nearest even
+    s = s16.astype(np.float32)[:, :, None]
+
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = xr / s                                                   # IEEE fp32 division
+    q = np.rint(t)                                                   # ties to even
+    q = np.clip(q, -qmax[None, :, None], qmax[None, :, None])
+    q = np.where(s == 0.0, 0.0, q)
+    return q.astype(np.int8).reshape(rows, K), np.ascontiguousarray(s16.T)
+
+
+# --------------------------------------------------------------------------- step: pack / unpack
+def pack_rows(codes: np.ndarray) -> np.ndarray:
+    """int8 codes [rows, K] -> packed bytes [rows, (K-128)/2 + 128]."""
+    codes = np.asarray(codes, dtype=np.int8)
+    rows, K = codes.shape
+    klo = K - OUTLIERS
+    u = codes.view(np.uint8)
+    lo = u[:, 0:klo:2] & 0x0F                  # even index -> low nibble
+    hi = u[:, 1:klo:2] & 0x0F                  # odd index  -> high nibble
+    body = (lo | (hi << 4)).astype(np.uint8)
+    tail = u[:, klo:]
+    return np.ascontiguousarray(np.concatenate([body, tail], axis=1))
+
+
+def unpack_rows(packed: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of :func:`pack_rows`."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    rows = packed.shape[0]
+    if packed.shape[1] != row_bytes(K):
+        raise ValueError("packed row length does not match K")
+    klo = K - OUTLIERS
+    body = packed[:, : klo // 2].astype(np.int16)
+    lo = body & 0x0F
+    hi = body >> 4
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty((rows, K), dtype=np.int8)
+    out[:, 0:klo:2] = lo
+    out[:, 1:klo:2] = hi
+    out[:, klo:] = packed[:, klo // 2:].view(np.int8)
+    return out
+
+
+# --------------------------------------------------------------------------- the layer's two runtime calls
+def quantize_act(X: np.ndarray, perm: np.ndarray):
+    """Runtime activation quantize: (packed codes u8 [M, row_bytes], scales fp16 [G, M])."""
+    q, s = quantize_rows(X, perm)
+    return pack_rows(q), s
+
+
+def pack_weights(W: np.ndarray, perm: np.ndarray):
+    """Offline weight pack with the same rule: (packed u8 [N, row_bytes], scales fp16 [G, N])."""
+    q, s = quantize_rows(W, perm)
+    return pack_rows(q), s
+
+
+# --------------------------------------------------------------------------- step: per-group integer products
+def group_acc(qx: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """acc[g, m, n] = sum over the 128 channels k of group g of qx[m, k] * qw[n, k].
+
+    Computed with an fp64 matmul per group: every partial sum is an integer of magnitude
+    at most 128 * 127 * 127 < 2**53, so the fp64 result is exact; it is checked to be
+    integral and to fit in int32."""
+    qx = np.asarray(qx, dtype=np.int8)
+    qw = np.asarray(qw, dtype=np.int8)
+    M, K = qx.shape
+    N = qw.shape[0]
+    G = num_groups(K)
+    out = np.empty((G, M, N), dtype=np.int64)
+    for g in range(G):
+        a = qx[:, g * GROUP:(g + 1) * GROUP].astype(np.float64)
+        b = qw[:, g * GROUP:(g + 1) * GROUP].astype(np.float64)
+        p = a @ b.T
+        ip = p.astype(np.int64)
+        if not np.array_equal(ip.astype(np.float64), p):
+            raise AssertionError("non-integral group product")
+        out[g] = ip
+    if np.abs(out).max(initial=0) >= 2 ** 31:
+        raise AssertionError("group product overflows int32")
+    return out
+
+
+# --------------------------------------------------------------------------- step: dequantised output
+def _expand(scales: np.ndarray, K: int) -> np.ndarray:
+    """fp16 scales [G, rows] -> fp64 [rows, K] (each scale repeated over its 128 channels)."""
+    return np.repeat(np.asarray(scales, dtype=np.float16).astype(np.float64).T, GROUP, axis=1)[:, :K]
+
+
+def gemm_ref(qx: np.ndarray, sx: np.ndarray, qw: np.ndarray, sw: np.ndarray) -> np.ndarray:
+    """Y64[m, n] = sum_g acc_g[m, n] * sx[g, m] * sw[g, n] in fp64.
+
+    Written as one fp64 matmul of the dequantised operands: each product q * s is exact in
+    fp64, so this is the same sum up to fp64 rounding order."""
+    K = qx.shape[1]
+    a = qx.astype(np.float64) * _expand(sx, K)
+    b = qw.astype(np.float64) * _expand(sw, K)
+    return a @ b.T
+
+
+def gemm_ref_grouped(qx, sx, qw, sw) -> np.ndarray:
+    """The same output written as the explicit sum over groups of scaled integer products."""
+    acc = group_acc(qx, qw).astype(np.float64)
+    sxd = np.asarray(sx, dtype=np.float16).astype(np.float64)
+    swd = np.asarray(sw, dtype=np.float16).astype(np.float64)
+    y = np.zeros(acc.shape[1:], dtype=np.float64)
+    for g in range(acc.shape[0]):
+        y += acc[g] * sxd[g][:, None] * swd[g][None, :]
+    return y
+
+
+def to_fp16(y64: np.ndarray) -> np.ndarray:
+    """Round fp64 to fp16, nearest even."""
+    return np.asarray(y64, dtype=np.float64).astype(np.float16)
+
+
+def linear(X: np.ndarray, W: np.ndarray, perm: np.ndarray):
+    """Whole layer: returns (Y fp16, Y64, (Xq, sx), (Wq, sw))."""
+    qx, sx = quantize_rows(X, perm)
+    qw, sw = quantize_rows(W, perm)
+    y64 = gemm_ref(qx, sx, qw, sw)
+    return to_fp16(y64), y64, (pack_rows(qx), sx), (pack_rows(qw), sw)
+
+
+def effective_bits(K: int, scale_bytes: int = 2) -> float:
+    """Bits per element of one quantized row including its per-group scales."""
+    return (row_bytes(K) * 8 + num_groups(K) * scale_bytes * 8) / K
