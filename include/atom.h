@@ -1,0 +1,133 @@
+/*
+ * atom.h -- C ABI of the MI355X (gfx950) W4A4 mixed-precision quantized linear layer.
+ *
+ * The layer (Atom: "Low-bit Quantization for Efficient and Accurate LLM Serving"):
+ *   - a fixed set of 128 outlier input channels is moved to the tail of every row and kept
+ *     as one INT8 group (quantization record, Fields "Bits", "Activation scheme", "notes":
+ *     a 128-channel high-precision group);
+ *   - the dense bulk is quantized to INT4 with an independent scale per contiguous group of
+ *     128 elements (record, Field "Weight group size" and "notes"; summary page, method
+ *     paragraph: per-group scales);
+ *   - the product runs on integer operators (index page, Abstract; record, "notes"): one
+ *     exact integer dot product per 128-channel group, scaled in fp32 and summed.
+ *
+ * Conventions for every call below
+ *   - Every tensor pointer is a DEVICE pointer into memory the caller owns.  The library
+ *     never allocates, frees or synchronizes; work is enqueued on `stream` (a hipStream_t;
+ *     NULL = the default stream) and the call returns.  Inputs are only read, outputs are
+ *     fully overwritten.
+ *   - Dense row-major layouts.  Pointers must be 16-byte aligned (ATOM_E_ALIGN otherwise).
+ *   - Shapes: K is a multiple of 128 with 256 <= K <= ATOM_MAX_K; rows (M, N) >= 1 and
+ *     <= ATOM_MAX_ROWS.  G = K/128 groups: groups 0..G-2 are INT4, group G-1 is the INT8
+ *     outlier group.  RB = atom_row_bytes(K) = (K-128)/2 + 128 bytes per packed row.
+ *   - Packed row format: byte j < (K-128)/2 holds reordered codes 2j (low nibble) and 2j+1
+ *     (high nibble) as 4-bit two's complement in [-7, 7]; the last 128 bytes hold the INT8
+ *     outlier codes in [-127, 127].  Scales are fp16, group-major [G, rows].
+ *   - Argument checks run on the host before any HIP call and return the status without
+ *     enqueuing anything.  A failed launch returns ATOM_E_HIP.  Faults inside a kernel
+ *     surface at the caller's next synchronization.  Calls that share no output buffer may
+ *     run concurrently on different streams.
+ */
+#ifndef ATOM_H_
+#define ATOM_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATOM_GROUP 128        /* elements per quantization group (record, "Weight group size") */
+#define ATOM_OUTLIERS 128     /* high-precision outlier channels (record, "notes") */
+#define ATOM_MAX_K 32768      /* largest K the kernels stage in LDS */
+#define ATOM_MAX_ROWS (1 << 24)
+
+enum {
+  ATOM_OK = 0,
+  ATOM_E_NULL = 1,     /* a required pointer is NULL */
+  ATOM_E_SHAPE = 2,    /* K not a multiple of 128, K < 256 or > ATOM_MAX_K, rows out of range */
+  ATOM_E_ALIGN = 3,    /* a pointer is not 16-byte aligned */
+  ATOM_E_OVERLAP = 4,  /* an output range overlaps an input or another output range */
+  ATOM_E_HIP = 5       /* the HIP runtime reported an error when enqueuing */
+};
+
+/* Bytes of one packed row, (K-128)/2 + 128; or -ATOM_E_SHAPE for an invalid K. */
+int64_t atom_row_bytes(int32_t K);
+
+/* Number of 128-channel groups, K/128; or -ATOM_E_SHAPE for an invalid K. */
+int32_t atom_num_groups(int32_t K);
+
+/* Static description of a status code; never NULL. */
+const char *atom_strerror(int status);
+
+/*
+ * Outlier statistic (offline).  stat[c] = sum over m < M of X[m,c]^2 for every input
+ * channel c of fp16 calibration activations X [M, K], returned as the exact sum rounded
+ * once to fp64 (round to nearest even), so the value does not depend on summation order.
+ * The pages leave the selection statistic open (record, "Activation scheme": a small set of
+ * outlier channels kept at higher precision); this is the statistic the layer uses.
+ *   X    : const fp16 [M, K]
+ *   stat : double [K]                       (output)
+ */
+int atom_channel_stat(const void *X, int32_t M, int32_t K, double *stat, void *stream);
+
+/*
+ * Outlier selection and reorder (offline).  The 128 channels with the largest stat are the
+ * outliers (ties go to the lower channel index).  perm lists the non-outlier channels in
+ * ascending order followed by the outlier channels in ascending order: reordered channel j
+ * takes original channel perm[j], so the outliers form the tail group G-1 (record, "notes":
+ * one 128-channel high-precision group).  stat must hold no NaN.
+ *   stat : const double [K]
+ *   perm : int32 [K]                        (output)
+ */
+int atom_select_outliers(const double *stat, int32_t K, int32_t *perm, void *stream);
+
+/*
+ * Offline weight pack (summary page, method paragraph: weights grouped into small blocks
+ * with per-group scales).  Row n of W is reordered through perm and quantized group by
+ * group exactly as atom_quantize_act does for a token row.
+ *   W    : const fp16 [N, K]      perm : const int32 [K], a permutation of 0..K-1
+ *   Wq   : uint8 [N, RB]          sw   : fp16 [G, N]          (outputs)
+ * Entries of perm outside 0..K-1 are clamped into range (garbage out, no fault).
+ */
+int atom_pack_weights(const void *W, const int32_t *perm, int32_t N, int32_t K,
+                      void *Wq, void *sw, void *stream);
+
+/*
+ * Runtime activation quantize (record, "Activation scheme": dense bulk 4-bit, outlier
+ * channels at higher precision; summary page: a dedicated outlier path).  For every token
+ * row m and group g of the reordered row x = X[m, perm]:
+ *   a = max |x| over the group;  qmax = 7 (g < G-1) or 127 (g = G-1);
+ *   s = fp16_rne(fp32(a / qmax));  code = clamp(rint_even(fp32(x / s)), -qmax, qmax),
+ *   code = 0 where s == 0.
+ *   X    : const fp16 [M, K]      perm : const int32 [K]
+ *   Xq   : uint8 [M, RB]          sx   : fp16 [G, M]           (outputs)
+ */
+int atom_quantize_act(const void *X, const int32_t *perm, int32_t M, int32_t K,
+                      void *Xq, void *sx, void *stream);
+
+/*
+ * W4A4 GEMM (index page, Abstract: low-bit integer operators; record, "notes": integer
+ * path).  Y[m,n] = fp16_rne( sum_g acc_g[m,n] * sx[g,m] * sw[g,n] ) where
+ * acc_g[m,n] = sum over the 128 channels of group g of code_x * code_w is an exact integer;
+ * the scale products and the sum over groups are fp32.
+ *   Xq : const uint8 [M, RB]   sx : const fp16 [G, M]
+ *   Wq : const uint8 [N, RB]   sw : const fp16 [G, N]
+ *   Y  : fp16 [M, N]                                           (output)
+ */
+int atom_gemm(const void *Xq, const void *sx, const void *Wq, const void *sw,
+              int32_t M, int32_t N, int32_t K, void *Y, void *stream);
+
+/*
+ * Per-group integer accumulators (verification aid): acc[g, m, n] = acc_g[m,n] as defined
+ * for atom_gemm, computed by the same main loop.  acc is int32 [G, M, N] (output,
+ * G*M*N*4 bytes).
+ */
+int atom_gemm_group_acc(const void *Xq, const void *Wq, int32_t M, int32_t N, int32_t K,
+                        int32_t *acc, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATOM_H_ */

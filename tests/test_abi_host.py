@@ -1,0 +1,150 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is ever launched).
+
+The library must load, export every function declared in include/atom.h, and reject every
+invalid argument on the host before it touches the HIP runtime.  The calls below pass fake
+(never dereferenced) addresses and always fail validation, so nothing is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_gemm_amd as bq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "atom.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_OVERLAP, E_HIP = 0, 1, 2, 3, 4, 5
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(atom_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bq.lib_path()):
+        pytest.skip("libatom.so not built (python -m bit_quantized_gemm_amd.build)")
+    return bq.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) == 9
+    assert sorted(bq.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_constants():
+    text = open(HEADER).read()
+    assert re.search(r"#define ATOM_GROUP 128\b", text)
+    assert re.search(r"#define ATOM_OUTLIERS 128\b", text)
+    assert re.search(rf"#define ATOM_MAX_K {bq.MAX_K}\b", text)
+
+
+def test_shape_helpers(lib):
+    assert bq.atom_row_bytes(4096) == 2112
+    assert bq.atom_row_bytes(11008) == 5568
+    assert bq.atom_row_bytes(256) == 192
+    assert bq.atom_num_groups(4096) == 32
+    assert bq.atom_num_groups(11008) == 86
+    for bad in (0, 128, 200, 4100, 32768 + 128, -256):
+        assert bq.atom_row_bytes(bad) == -E_SHAPE
+        assert bq.atom_num_groups(bad) == -E_SHAPE
+    assert bq.atom_row_bytes(32768) == (32768 - 128) // 2 + 128
+
+
+def test_strerror(lib):
+    for s in (OK, E_NULL, E_SHAPE, E_ALIGN, E_OVERLAP, E_HIP, 99):
+        msg = bq.atom_strerror(s)
+        assert isinstance(msg, str) and msg
+    assert bq.atom_strerror(OK) == "ok"
+
+
+A = 0x10000000          # fake, aligned, disjoint device addresses (never dereferenced)
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+E = 0x50000000
+S = None                # default stream
+
+
+def _q(lib, X, perm, M, K, Q, Sc):
+    return lib.atom_quantize_act(X, perm, M, K, Q, Sc, S)
+
+
+def test_quantize_validation(lib):
+    assert _q(lib, None, B, 4, 256, C, D) == E_NULL
+    assert _q(lib, A, None, 4, 256, C, D) == E_NULL
+    assert _q(lib, A, B, 4, 256, None, D) == E_NULL
+    assert _q(lib, A, B, 4, 256, C, None) == E_NULL
+    for K in (0, 128, 300, 32896):
+        assert _q(lib, A, B, 4, K, C, D) == E_SHAPE
+    for M in (0, -1, (1 << 24) + 1):
+        assert _q(lib, A, B, M, 256, C, D) == E_SHAPE
+    assert _q(lib, A + 8, B, 4, 256, C, D) == E_ALIGN
+    assert _q(lib, A, B + 4, 4, 256, C, D) == E_ALIGN
+    assert _q(lib, A, B, 4, 256, C + 2, D) == E_ALIGN
+    assert _q(lib, A, B, 4, 256, C, D + 1) == E_ALIGN
+    # Q starts inside X (X spans 4*256*2 = 2048 bytes)
+    assert _q(lib, A, B, 4, 256, A + 1024, D) == E_OVERLAP
+    # S overlaps perm (perm spans 1024 bytes)
+    assert _q(lib, A, B, 4, 256, C, B + 512) == E_OVERLAP
+    # S overlaps Q (Q spans 4*192 = 768 bytes)
+    assert _q(lib, A, B, 4, 256, C, C + 512) == E_OVERLAP
+    # same checks on the weight entry point
+    assert lib.atom_pack_weights(A, B, 4, 300, C, D, S) == E_SHAPE
+    assert lib.atom_pack_weights(A, None, 4, 256, C, D, S) == E_NULL
+
+
+def test_gemm_validation(lib):
+    g = lib.atom_gemm
+    assert g(None, B, C, D, 4, 4, 256, E, S) == E_NULL
+    assert g(A, B, C, D, 4, 4, 256, None, S) == E_NULL
+    assert g(A, B, C, D, 0, 4, 256, E, S) == E_SHAPE
+    assert g(A, B, C, D, 4, 0, 256, E, S) == E_SHAPE
+    assert g(A, B, C, D, 4, 4, 384 + 64, E, S) == E_SHAPE
+    assert g(A, B, C, D + 2, 4, 4, 256, E, S) == E_ALIGN
+    assert g(A, B, C, D, 4, 4, 256, A + 16, S) == E_OVERLAP     # Y inside Xq
+    assert g(A, B, C, D, 4, 4, 256, D, S) == E_OVERLAP          # Y on sw
+    ga = lib.atom_gemm_group_acc
+    assert ga(A, None, 4, 4, 256, E, S) == E_NULL
+    assert ga(A, C, 4, 4, 200, E, S) == E_SHAPE
+    assert ga(A, C, 4, 4, 256, E + 4, S) == E_ALIGN
+    assert ga(A, C, 4, 4, 256, C + 64, S) == E_OVERLAP
+
+
+def test_select_validation(lib):
+    assert lib.atom_channel_stat(None, 4, 256, B, S) == E_NULL
+    assert lib.atom_channel_stat(A, 0, 256, B, S) == E_SHAPE
+    assert lib.atom_channel_stat(A, 4, 256, B + 8, S) == E_ALIGN
+    assert lib.atom_channel_stat(A, 4, 256, A + 16, S) == E_OVERLAP
+    assert lib.atom_select_outliers(None, 256, B, S) == E_NULL
+    assert lib.atom_select_outliers(A, 100, B, S) == E_SHAPE
+    assert lib.atom_select_outliers(A, 256, A + 1024, S) == E_OVERLAP
+
+
+def test_binding_refuses_host_tensors():
+    """The product path has no CPU fallback: host tensors are refused before any call."""
+    torch = pytest.importorskip("torch")
+    X = torch.zeros((4, 256), dtype=torch.float16)
+    perm = torch.arange(256, dtype=torch.int32)
+    if not os.path.exists(bq.lib_path()):
+        with pytest.raises(bq.AtomError):
+            bq.atom_quantize_act(X, perm)
+        return
+    with pytest.raises(bq.AtomError, match="ROCm device"):
+        bq.atom_quantize_act(X, perm)
+    with pytest.raises(bq.AtomError, match="ROCm device"):
+        bq.atom_channel_stat(X)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(bq, "_LIB", None)
+    monkeypatch.setenv("ATOM_LIB", str(tmp_path / "nope.so"))
+    with pytest.raises(bq.AtomError, match="not built"):
+        bq.load_library()

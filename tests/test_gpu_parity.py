@@ -1,0 +1,274 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Bar: outlier statistic, perm, packed INT4/INT8 codes, fp16 scales and the per-group int32
+accumulators are bit-exact; the fp16 output Y is within max(2e-3*|Y64|, 1e-2) of the
+oracle's fp64 value.  Every input comes from ``synth`` (seeded); every expected value
+from ``oracle``.  Calls go through the C ABI via the ctypes binding.
+"""
+import functools
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import atom_oracle as O
+
+torch = pytest.importorskip("torch")
+import bit_quantized_gemm_amd as bq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RTOL, ATOL = 2e-3, 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU visible")
+    bq.load_library()           # fails loudly if the HIP library is missing
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_y_close(y16, y64, what):
+    y = y16.astype(np.float64)
+    err = np.abs(y - y64)
+    tol = np.maximum(RTOL * np.abs(y64), ATOL)
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; "
+                           f"worst err {err.max():.3g} at {np.unravel_index(err.argmax(), err.shape)}")
+
+
+# --------------------------------------------------------------------------- workload cache
+@functools.lru_cache(maxsize=2)
+def workload(key):
+    w = synth.get(key)
+    _say(f"[inputs] {key} {w.name}")
+    x, wt, _ = synth.make_inputs(w)
+    perm = O.outlier_perm(x)
+    return w, x, wt, perm
+
+
+# --------------------------------------------------------------------------- a0: statistic + selection
+@pytest.mark.parametrize("key", ["T", "A", "B", "C"])
+def test_channel_stat_and_perm_bitexact(key):
+    w, x, _, perm = workload(key)
+    _say(f"[a0] {key} M={w.M} K={w.K}")
+    X = dev(x.view(np.float16))
+    stat = bq.atom_channel_stat(X)
+    p = bq.atom_select_outliers(stat)
+    st_ref = O.channel_stat(x)
+    np.testing.assert_array_equal(host(stat).view(np.uint64), st_ref.view(np.uint64))
+    np.testing.assert_array_equal(host(p), perm)
+
+
+def test_select_ties_and_order():
+    """Ties go to the lower channel index; the perm is a stable partition."""
+    K = 1024
+    stat = np.zeros(K)
+    stat[::3] = 2.0                     # 342 tied channels
+    stat[5] = 7.0
+    p = bq.atom_select_outliers(dev(stat))
+    ref = O.make_perm(K, O.select_outliers(stat))
+    np.testing.assert_array_equal(host(p), ref)
+
+
+# --------------------------------------------------------------------------- a1/a2: quantize
+def _check_rows(x, perm, q_dev, s_dev, rows=None, what=""):
+    xs = x if rows is None else x[rows]
+    qr, sr = O.quantize_rows(xs, perm)
+    q = host(q_dev)
+    s = host(s_dev)
+    if rows is not None:
+        q = q[rows]
+        s = s[:, rows]
+    np.testing.assert_array_equal(q, O.pack_rows(qr), err_msg=f"{what} codes")
+    np.testing.assert_array_equal(s.view(np.uint16), sr.view(np.uint16), err_msg=f"{what} scales")
+
+
+@pytest.mark.parametrize("key", ["T", "A", "B", "C"])
+def test_quantize_act_bitexact(key):
+    w, x, _, perm = workload(key)
+    _say(f"[a2] {key}")
+    Xq, sx = bq.atom_quantize_act(dev(x), dev(perm))
+    _check_rows(x, perm, Xq, sx, what=f"{key} activations")
+
+
+@pytest.mark.parametrize("key", ["T", "A", "B", "C"])
+def test_pack_weights_bitexact(key):
+    w, _, wt, perm = workload(key)
+    _say(f"[a1] {key}")
+    Wq, sw = bq.atom_pack_weights(dev(wt), dev(perm))
+    _check_rows(wt, perm, Wq, sw, what=f"{key} weights")
+
+
+def test_quantize_only_8192_bitexact():
+    """The standalone 8192x8192 activation quantize (128 channels x30)."""
+    x, _, _ = synth.quant_only_x()
+    _say("[a2] Dq 8192x8192")
+    perm = O.outlier_perm(x[:2048])     # calibration on a prefix keeps the oracle quick
+    Xq, sx = bq.atom_quantize_act(dev(x), dev(perm))
+    _check_rows(x, perm, Xq, sx, what="Dq")
+
+
+def test_golden_rows_on_gpu():
+    """The hand-worked rows of tests/golden/worked_rows.json, quantized on the GPU."""
+    fx = json.load(open(os.path.join(GOLDEN, "worked_rows.json")))
+    K = fx["K"]
+    X = np.zeros((len(fx["rows"]), K), dtype=np.float16)
+    for r, row in enumerate(fx["rows"]):
+        for c, hx in row["x_fp16_hex"].items():
+            X[r, int(c)] = np.array([int(hx, 16)], np.uint16).view(np.float16)[0]
+    Xq, sx = bq.atom_quantize_act(dev(X), dev(np.arange(K, dtype=np.int32)))
+    q, s = host(Xq), host(sx)
+    for r, row in enumerate(fx["rows"]):
+        assert s[:, r].view(np.uint16).tolist() == [int(h, 16) for h in row["scales_fp16_hex"]], row["name"]
+        exp = np.zeros(O.row_bytes(K), np.uint8)
+        for c, hx in row["packed_hex"].items():
+            exp[int(c) if int(c) < 128 else int(c) - 128 + (K - 128) // 2] = int(hx, 16)
+        np.testing.assert_array_equal(q[r], exp, err_msg=row["name"])
+
+
+# --------------------------------------------------------------------------- a3/a4: group accumulators
+@pytest.mark.parametrize("key", ["T", "A"])
+def test_group_acc_bitexact(key):
+    w, x, wt, perm = workload(key)
+    _say(f"[acc] {key}")
+    qx, _ = O.quantize_rows(x, perm)
+    qw, _ = O.quantize_rows(wt, perm)
+    Xq, _ = bq.atom_quantize_act(dev(x), dev(perm))
+    Wq, _ = bq.atom_pack_weights(dev(wt), dev(perm))
+    acc = host(bq.atom_gemm_group_acc(Xq, Wq, w.K))
+    np.testing.assert_array_equal(acc, O.group_acc(qx, qw))
+
+
+# --------------------------------------------------------------------------- a5: output
+@pytest.mark.parametrize("key", ["T", "A"])
+def test_gemm_full_output(key):
+    w, x, wt, perm = workload(key)
+    _say(f"[Y] {key} full")
+    Wq, sw = bq.atom_pack_weights(dev(wt), dev(perm))
+    Y = host(bq.linear(dev(x), dev(perm), Wq, sw))
+    _, y64, _, _ = O.linear(x, wt, perm)
+    assert_y_close(Y, y64, key)
+
+
+@pytest.mark.parametrize("key", ["B", "C"])
+def test_gemm_sampled_output(key):
+    w, x, wt, perm = workload(key)
+    _say(f"[Y] {key} sampled")
+    Wq, sw = bq.atom_pack_weights(dev(wt), dev(perm))
+    Y = host(bq.linear(dev(x), dev(perm), Wq, sw))
+    rng = np.random.default_rng(123)
+    rows = np.sort(rng.choice(w.M, 256, replace=False))
+    cols = np.sort(rng.choice(w.N, 1024, replace=False))
+    qx, sx = O.quantize_rows(x[rows], perm)
+    qw, sw_ref = O.quantize_rows(wt[cols], perm)
+    y64 = O.gemm_ref(qx, sx, qw, sw_ref)
+    assert_y_close(Y[np.ix_(rows, cols)], y64, key)
+
+
+def test_gemm_llama70b_sampled():
+    """Llama-70B MLP shape M=4096, K=8192, N=28672: codes of sampled rows bit-exact, Y sampled."""
+    w = synth.get("D")
+    _say("[Y] D sampled")
+    x, wt, _ = synth.make_inputs(w)
+    perm = O.outlier_perm(x[:1024])
+    Xd, Pd = dev(x), dev(perm)
+    Wq, sw = bq.atom_pack_weights(dev(wt), Pd)
+    Xq, sx = bq.atom_quantize_act(Xd, Pd)
+    Y = bq.atom_gemm(Xq, sx, Wq, sw, w.K)
+    rng = np.random.default_rng(7)
+    rows = np.sort(rng.choice(w.M, 256, replace=False))
+    cols = np.sort(rng.choice(w.N, 1024, replace=False))
+    _check_rows(x, perm, Xq, sx, rows=rows, what="D activations")
+    _check_rows(wt, perm, Wq, sw, rows=cols, what="D weights")
+    qx, sxr = O.quantize_rows(x[rows], perm)
+    qw, swr = O.quantize_rows(wt[cols], perm)
+    assert_y_close(host(Y)[np.ix_(rows, cols)], O.gemm_ref(qx, sxr, qw, swr), "D")
+
+
+# --------------------------------------------------------------------------- ragged / edge shapes
+RAGGED = [(1, 1, 256), (2, 3, 256), (37, 200, 384), (130, 129, 1152), (257, 513, 640), (16, 512, 1024),
+          (128, 128, 256), (129, 255, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", RAGGED)
+def test_ragged_shapes(M, N, K):
+    _say(f"[ragged] M={M} N={N} K={K}")
+    x, wt, _ = synth.make_linear(M, K, N, seed=M + N + K)
+    perm = np.random.default_rng(K).permutation(K).astype(np.int32)
+    Xd, Wd, Pd = dev(x), dev(wt), dev(perm)
+    Xq, sx = bq.atom_quantize_act(Xd, Pd)
+    Wq, sw = bq.atom_pack_weights(Wd, Pd)
+    Y = bq.atom_gemm(Xq, sx, Wq, sw, K)
+    acc = bq.atom_gemm_group_acc(Xq, Wq, K)
+    qx, sxr = O.quantize_rows(x, perm)
+    qw, swr = O.quantize_rows(wt, perm)
+    np.testing.assert_array_equal(host(Xq), O.pack_rows(qx))
+    np.testing.assert_array_equal(host(Wq), O.pack_rows(qw))
+    np.testing.assert_array_equal(host(sx).view(np.uint16), sxr.view(np.uint16))
+    np.testing.assert_array_equal(host(acc), O.group_acc(qx, qw))
+    assert_y_close(host(Y), O.gemm_ref(qx, sxr, qw, swr), f"{M}x{N}x{K}")
+
+
+def test_zero_and_degenerate_rows():
+    M, N, K = 64, 96, 512
+    x, wt, _ = synth.make_linear(M, K, N, seed=9)
+    x[3] = 0                                   # all-zero token
+    x[5, :] = np.float16(2.0 ** -24)           # scales underflow to zero
+    x[7, :128] = np.float16(1e-6)              # subnormal scale in group 0
+    wt[10] = 0                                 # all-zero weight row
+    perm = np.arange(K, dtype=np.int32)
+    Xq, sx = bq.atom_quantize_act(dev(x), dev(perm))
+    Wq, sw = bq.atom_pack_weights(dev(wt), dev(perm))
+    Y = host(bq.atom_gemm(Xq, sx, Wq, sw, K))
+    y16, y64, (xq_r, sx_r), (wq_r, sw_r) = O.linear(x, wt, perm)
+    np.testing.assert_array_equal(host(Xq), xq_r)
+    np.testing.assert_array_equal(host(sx).view(np.uint16), sx_r.view(np.uint16))
+    np.testing.assert_array_equal(host(Wq), wq_r)
+    assert np.all(Y[3] == 0) and np.all(Y[5] == 0) and np.all(Y[:, 10] == 0)
+    assert_y_close(Y, y64, "degenerate")
+
+
+def test_max_k():
+    M, N, K = 8, 40, bq.MAX_K
+    x, wt, _ = synth.make_linear(M, K, N, seed=1)
+    perm = np.random.default_rng(2).permutation(K).astype(np.int32)
+    Xq, sx = bq.atom_quantize_act(dev(x), dev(perm))
+    Wq, sw = bq.atom_pack_weights(dev(wt), dev(perm))
+    Y = host(bq.atom_gemm(Xq, sx, Wq, sw, K))
+    qx, sxr = O.quantize_rows(x, perm)
+    qw, swr = O.quantize_rows(wt, perm)
+    np.testing.assert_array_equal(host(Xq), O.pack_rows(qx))
+    assert_y_close(Y, O.gemm_ref(qx, sxr, qw, swr), "max K")
+
+
+# --------------------------------------------------------------------------- determinism and streams
+def test_deterministic_and_side_stream():
+    w, x, wt, perm = workload("A")
+    Xd, Pd = dev(x), dev(perm)
+    Wq, sw = bq.atom_pack_weights(dev(wt), Pd)
+    y1 = host(bq.linear(Xd, Pd, Wq, sw))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y2 = bq.linear(Xd, Pd, Wq, sw, stream=s)
+    s.synchronize()
+    y2 = host(y2)
+    np.testing.assert_array_equal(y1.view(np.uint16), y2.view(np.uint16))
