@@ -37,6 +37,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
 WORKLOAD_SETS = {
     "llama7b": ["A", "B", "C"],
     "A": ["A"], "B": ["B"], "C": ["C"], "D": ["D"],
+    "Dq": [],              # activation quantize alone on 8192 x 8192 fp16 (128 outlier channels x30)
 }
 
 
@@ -118,6 +119,50 @@ def cpu_baseline(shapes, budget_rows):
             "seconds": round(secs, 3)}
 
 
+def quant_only(args, torch, bq, synth, dev, R):
+    """Activation-quantize throughput on the 8192 x 8192 workload (HBM-bound kernel)."""
+    x, _, _ = synth.quant_only_x()
+    M, K = x.shape
+    X0 = torch.from_numpy(x).to(dev)
+    perm = bq.atom_select_outliers(bq.atom_channel_stat(X0))
+    copies = []
+    for r in range(R):
+        Xr = X0.clone() if r == 0 else (X0 * (1.0 + 1e-3 * r)).to(torch.float16)
+        copies.append(dict(X=Xr, Xq=torch.empty((M, bq.atom_row_bytes(K)), dtype=torch.uint8, device=dev),
+                           sx=torch.empty((K // 128, M), dtype=torch.float16, device=dev)))
+    del X0
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        c = copies[i % R]
+        bq.atom_quantize_act(c["X"], perm, Xq=c["Xq"], sx=c["sx"], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    qb = quant_bytes(M, K)
+    gbs = qb / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "activation quantize throughput (reorder + per-group absmax + INT4 pack + INT8 tail)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16->int4/int8", "data": "synthetic",
+        "config": {"workload": "quantize_only_8192x8192", "M": M, "K": K, "rotating_input_copies": R},
+        "roofline": {"kernel": "row_quantize_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": qb, "avg_launch_us": round(ms * 1e3, 3)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +191,8 @@ def main():
     dev = torch.device("cuda:0")
     keys = WORKLOAD_SETS[args.workload]
     R = max(1, args.rotate)
+    if args.workload == "Dq":
+        return quant_only(args, torch, bq, synth, dev, R)
 
     # ---------------------------------------------------------------- offline: inputs, perm, weight pack
     sets = []

@@ -162,7 +162,7 @@ __device__ __forceinline__ void store_stage_int8(const StageRegs<APER, BPER>& st
 
 // kAcc = false: Y output.  kAcc = true: write the per-group integer accumulators instead.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool kAcc>
-__global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a4_kernel(
+__global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(4))) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx, const uint8_t* __restrict__ Wq,
     const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out) {
   using T = Tile<BM, BN, WAVES_M, WAVES_N>;
@@ -284,6 +284,48 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
     }
   };
 
+  // Tile row i of an INT4 group (tiles (i, 0..kTN-1)): four K=32 MFMAs per tile.
+  auto mma_int4_row = [&](int buf, int i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const v4i af = lds_a_word(buf, i, h, w);
+#pragma unroll
+        for (int j = 0; j < T::kTN; ++j) {
+          const v4i bf = lds_b_word(buf, j, h, w);
+          acc[i][j] = (h == 0 && w == 0) ? mma_i8_first(af, bf) : mma_i8(af, bf, acc[i][j]);
+        }
+      }
+  };
+
+  // fp16 scale operands of one group for this lane: K column 0 of A holds sx (lanes < 32),
+  // K row 0 of B holds sw.
+  auto read_scales = [&](int buf, h4 (&sa)[T::kTM], h4 (&sb)[T::kTN]) {
+#pragma unroll
+    for (int i = 0; i < T::kTM; ++i) {
+      const uint16_t h = kh == 0 ? lds_sx[buf][wm * T::kWTM + i * 32 + l32] : (uint16_t)0;
+      sa[i] = h4{__builtin_bit_cast(_Float16, h), (_Float16)0, (_Float16)0, (_Float16)0};
+    }
+#pragma unroll
+    for (int j = 0; j < T::kTN; ++j) {
+      const uint16_t h = kh == 0 ? lds_sw[buf][wn * T::kWTN + j * 32 + l32] : (uint16_t)0;
+      sb[j] = h4{__builtin_bit_cast(_Float16, h), (_Float16)0, (_Float16)0, (_Float16)0};
+    }
+  };
+
+  // Epilogue of tile row i: yacc += float(acc) * (sx (x) sw); `outlier` scales the product by
+  // 256 so that every group's contribution carries the factor 256 of the widened groups.
+  auto epi_row = [&](int i, h4 sai, const h4 (&sb)[T::kTN], bool outlier) {
+#pragma unroll
+    for (int j = 0; j < T::kTN; ++j) {
+      v16f sp = __builtin_amdgcn_mfma_f32_32x32x8f16(sai, sb[j], v16f{}, 0, 0, 0);
+      if (outlier) sp *= 256.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) yacc[i][j][r] = __builtin_fmaf((float)acc[i][j][r], sp[r], yacc[i][j][r]);
+    }
+  };
+
   // Scale the finished integer accumulators of group g into the fp32 output accumulators,
   // or (kAcc) write them out.  `widened`: the accumulators carry the factor 256.
   auto epilogue = [&](int buf, int g, bool widened) {
@@ -328,21 +370,18 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   load_stage(st, ad, 1, G);
   __syncthreads();
 
-  // INT4 groups: stages 0 .. G-2
-  for (int s = 0; s < G - 1; ++s) {
-    const int buf = s & 1;
-    mma_int4(buf);
-    // stage s+1 into the other buffer (released by the last barrier), then start stage s+2
-    if (s + 1 < G - 1)
-      store_stage_int4<BM, BN, kAcc>(st, ad, lds_a[buf ^ 1], lds_b[buf ^ 1], lds_sx[buf ^ 1], lds_sw[buf ^ 1], tid);
-    else
-      store_stage_int8<BM, BN, kAcc>(st, ad, lds_a[buf ^ 1], lds_b[buf ^ 1], lds_sx[buf ^ 1], lds_sw[buf ^ 1], tid);
-    load_stage(st, ad, s + 2, G);                    // s+2 <= G: always a valid stage
-    epilogue(buf, s, true);
-    __syncthreads();
-  }
-  // INT8 outlier group: stages G-1 and G
   {
+    for (int s = 0; s < G - 1; ++s) {
+      const int buf = s & 1;
+      mma_int4(buf);
+      if (s + 1 < G - 1)
+        store_stage_int4<BM, BN, kAcc>(st, ad, lds_a[buf ^ 1], lds_b[buf ^ 1], lds_sx[buf ^ 1], lds_sw[buf ^ 1], tid);
+      else
+        store_stage_int8<BM, BN, kAcc>(st, ad, lds_a[buf ^ 1], lds_b[buf ^ 1], lds_sx[buf ^ 1], lds_sw[buf ^ 1], tid);
+      load_stage(st, ad, s + 2, G);                  // s+2 <= G: always a valid stage
+      epilogue(buf, s, true);
+      __syncthreads();
+    }
     const int buf = (G - 1) & 1;
     mma_int8(buf, true);
     store_stage_int8<BM, BN, kAcc>(st, ad, lds_a[buf ^ 1], lds_b[buf ^ 1], lds_sx[buf ^ 1], lds_sw[buf ^ 1], tid);
@@ -367,7 +406,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
 }
 
 // 128 x 128 workgroup tile, 2 x 2 waves of 64 x 64 (2 x 2 MFMA tiles of 32 x 32 each).
-constexpr int kBM = 128, kBN = 128, kWavesM = 2, kWavesN = 2;
+constexpr int kBM = 128, kBN = 128, kWavesM = 2, kWavesN = 4;
 
 }  // namespace
 

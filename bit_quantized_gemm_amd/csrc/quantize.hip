@@ -7,11 +7,14 @@
 // (Field "Bits": w4a4; "Weight group size": 128; "notes": each contiguous 128-element group is
 // quantized independently, plus one 128-channel high-precision group).
 //
-// Work layout: one 256-thread workgroup per row.  The fp16 row is staged in LDS with
-// 16-byte loads, then every thread gathers 8 consecutive reordered elements through perm
-// (a group of 128 is 16 neighbouring lanes), reduces the group absmax across those 16 lanes,
-// and writes its 8 codes as one 32-bit word (INT4) or 8 bytes (INT8 tail): each group's
-// 16 lanes store a contiguous 64- or 128-byte run.
+// Work layout.  Persistent workgroups of 256 threads walk the rows.  A row is staged in LDS
+// (fp16, 16-byte loads); the next row's loads are issued into registers before the current
+// row is processed, so HBM reads overlap the arithmetic.  The gather offsets through perm are
+// computed once per workgroup and kept in registers (no memory traffic in the row loop, so
+// nothing else waits behind the prefetch).  Each thread gathers 16 consecutive
+// reordered elements through perm; a group of 128 is 8 neighbouring lanes, whose absmax is
+// combined with DPP row operations.  Each thread writes its 16 codes as 8 bytes (INT4) or
+// 16 bytes (INT8 tail), so a group's 8 lanes store one contiguous 64- or 128-byte run.
 //
 // Exact codes without a per-element IEEE division: with r = 1/s correctly rounded,
 // t = x*r, e = fma(-t, s, x), u = fma(e, r, t), the integer nearest u (ties to even) equals
@@ -30,55 +33,98 @@
 namespace atom {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
-constexpr int kPerThread = 8;
+constexpr int kPerThread = 16;                       // reordered elements per thread per pass
+constexpr int kLanesPerGroup = ATOM_GROUP / kPerThread;   // 8
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+// max over the 8 lanes of a group (lanes 8k..8k+7) via DPP: xor 1, xor 2 (quad perms), then
+// the half-row mirror (lane i <-> 7-i), which pairs the two quads of the group.
+__device__ __forceinline__ float group_max8(float a) {
+  a = __builtin_fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false)));
+  a = __builtin_fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0x4E, 0xF, 0xF, false)));
+  a = __builtin_fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0x141, 0xF, 0xF, false)));
+  return a;
+}
 
 // Code of x for scale s (> 0) with reciprocal r, as the low byte of the returned word.
 __device__ __forceinline__ uint32_t code_bits(float x, float s, float r, float qmax) {
   const float t = x * r;
   const float e = __builtin_fmaf(-t, s, x);
   const float u = __builtin_fmaf(e, r, t);
-  const float v = __builtin_fminf(__builtin_fmaxf(u, -qmax), qmax);
+  const float v = __builtin_amdgcn_fmed3f(u, -qmax, qmax);
   return __float_as_uint(v + 12582912.0f);
 }
 
+// low bytes of a,b,c,d -> one word [a, b, c, d]
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);   // [a.b0, b.b0, 0, 0]
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x04000C0Cu);   // [0, 0, c.b0, d.b0]
+  return ab | cd;
+}
+
+// CHUNKS: 16-byte row chunks each thread prefetches (K <= CHUNKS * 2048).
+// PASSES: passes of 4096 reordered elements per row whose gather offsets stay in registers
+// for the whole kernel (K <= PASSES * 4096); 0 = read perm from memory on every row.
+template <int CHUNKS, int PASSES>
 __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* __restrict__ X,
                                                                 const int32_t* __restrict__ perm, int rows, int K,
                                                                 uint8_t* __restrict__ Q, uint16_t* __restrict__ S) {
-  extern __shared__ uint4 lds_row4[];
-  const uint16_t* lds_row = reinterpret_cast<const uint16_t*>(lds_row4);
-  const int row = blockIdx.x;
+  extern __shared__ u32x4 lds_row4[];
+  const uint8_t* lds_bytes = reinterpret_cast<const uint8_t*>(lds_row4);
   const int G = K / ATOM_GROUP;
   const int klo = K - ATOM_OUTLIERS;
   const size_t rb = (size_t)(klo / 2 + ATOM_OUTLIERS);
-
-  const uint4* src = reinterpret_cast<const uint4*>(X + (size_t)row * K);
-  for (int i = threadIdx.x; i < K / 8; i += kThreads) lds_row4[i] = src[i];
-  __syncthreads();
-
-  uint8_t* qrow = Q + (size_t)row * rb;
+  const int nchunks = K / 8;                         // 16-byte chunks per row
   const unsigned kmax = (unsigned)(K - 1);
-  for (int c = threadIdx.x * kPerThread; c < K; c += kThreads * kPerThread) {
+  constexpr int kPassElems = kThreads * kPerThread;  // 4096
+
+  // LDS byte offsets of this thread's 16 reordered elements (clamped: a bad perm gives
+  // garbage, never an out-of-range read)
+  auto gather_offsets = [&](int c, int (&off)[kPerThread]) {
+#pragma unroll
+    for (int v = 0; v < kPerThread / 4; ++v) {
+      const int4 p = *reinterpret_cast<const int4*>(perm + c + 4 * v);
+      off[4 * v] = 2 * (int)__builtin_elementwise_min((unsigned)p.x, kmax);
+      off[4 * v + 1] = 2 * (int)__builtin_elementwise_min((unsigned)p.y, kmax);
+      off[4 * v + 2] = 2 * (int)__builtin_elementwise_min((unsigned)p.z, kmax);
+      off[4 * v + 3] = 2 * (int)__builtin_elementwise_min((unsigned)p.w, kmax);
+    }
+  };
+  int offs[PASSES > 0 ? PASSES : 1][kPerThread];
+  if (PASSES > 0) {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int c = threadIdx.x * kPerThread + ps * kPassElems;
+      if (c < K) gather_offsets(c, offs[ps]);
+    }
+  }
+
+  u32x4 pre[CHUNKS];
+  auto prefetch = [&](int row) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(X + (size_t)row * K);
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      if (c < nchunks) pre[i] = src[c];
+    }
+  };
+
+  // Quantize the 16 reordered elements at position c (gather offsets off) of the LDS row.
+  auto quantize16 = [&](int c, const int (&off)[kPerThread], uint8_t* qrow, int row) {
     const int g = c / ATOM_GROUP;
     const bool tail = g == G - 1;
-    const int4 p0 = *reinterpret_cast<const int4*>(perm + c);
-    const int4 p1 = *reinterpret_cast<const int4*>(perm + c + 4);
-    const int pi[kPerThread] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
     float x[kPerThread];
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const unsigned idx = __builtin_elementwise_min((unsigned)pi[i], kmax);   // bad perm: clamp, no fault
-      x[i] = half_bits_to_float(lds_row[idx]);
+      x[i] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(lds_bytes + off[i]));
       a = __builtin_fmaxf(a, __builtin_fabsf(x[i]));
     }
-    // group absmax over the 16 lanes that share this group
-    a = __builtin_fmaxf(a, __shfl_xor(a, 1));
-    a = __builtin_fmaxf(a, __shfl_xor(a, 2));
-    a = __builtin_fmaxf(a, __shfl_xor(a, 4));
-    a = __builtin_fmaxf(a, __shfl_xor(a, 8));
+    a = group_max8(a);
 
     const float qmax = tail ? 127.0f : 7.0f;
     const __half s16 = __float2half_rn(a / qmax);      // correctly rounded fp32 divide, then RNE to fp16
@@ -93,27 +139,85 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
       for (int i = 0; i < kPerThread; ++i) b[i] = 0;
     }
     if (!tail) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int i = 0; i < kPerThread; ++i) w |= (b[i] & 0xfu) << (4 * i);
-      *reinterpret_cast<uint32_t*>(qrow + c / 2) = w;
-    } else {
+      // nibbles: even codes in the low nibble of each byte, odd codes in the high nibble
       uint2 w;
-      w.x = (b[0] & 0xff) | ((b[1] & 0xff) << 8) | ((b[2] & 0xff) << 16) | ((b[3] & 0xff) << 24);
-      w.y = (b[4] & 0xff) | ((b[5] & 0xff) << 8) | ((b[6] & 0xff) << 16) | ((b[7] & 0xff) << 24);
-      *reinterpret_cast<uint2*>(qrow + klo / 2 + (c - klo)) = w;
+      const uint32_t e0 = pack4(b[0], b[2], b[4], b[6]), o0 = pack4(b[1], b[3], b[5], b[7]);
+      const uint32_t e1 = pack4(b[8], b[10], b[12], b[14]), o1 = pack4(b[9], b[11], b[13], b[15]);
+      w.x = (e0 & 0x0F0F0F0Fu) | ((o0 << 4) & 0xF0F0F0F0u);
+      w.y = (e1 & 0x0F0F0F0Fu) | ((o1 << 4) & 0xF0F0F0F0u);
+      *reinterpret_cast<uint2*>(qrow + c / 2) = w;
+    } else {
+      u32x4 w;
+      w.x = pack4(b[0], b[1], b[2], b[3]);
+      w.y = pack4(b[4], b[5], b[6], b[7]);
+      w.z = pack4(b[8], b[9], b[10], b[11]);
+      w.w = pack4(b[12], b[13], b[14], b[15]);
+      *reinterpret_cast<u32x4*>(qrow + klo / 2 + (c - klo)) = w;
     }
-    if ((threadIdx.x & 15) == 0) S[(size_t)g * rows + row] = __half_as_ushort(s16);
+    if ((threadIdx.x & (kLanesPerGroup - 1)) == 0) S[(size_t)g * rows + row] = __half_as_ushort(s16);
+  };
+
+  int row = blockIdx.x;
+  if (row < rows) prefetch(row);
+  for (; row < rows; row += gridDim.x) {
+    __syncthreads();                                 // everyone finished reading the previous row
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      if (c < nchunks) lds_row4[c] = pre[i];
+    }
+    __syncthreads();
+    if (row + (int)gridDim.x < rows) prefetch(row + gridDim.x);   // next row's loads fly meanwhile
+
+    uint8_t* qrow = Q + (size_t)row * rb;
+    if (PASSES > 0) {
+#pragma unroll
+      for (int ps = 0; ps < (PASSES > 0 ? PASSES : 1); ++ps) {
+        const int c = threadIdx.x * kPerThread + ps * kPassElems;
+        if (c < K) quantize16(c, offs[ps], qrow, row);
+      }
+    } else {
+      for (int c = threadIdx.x * kPerThread; c < K; c += kPassElems) {
+        int off[kPerThread];
+        gather_offsets(c, off);
+        quantize16(c, off, qrow, row);
+      }
+    }
   }
+}
+
+template <int CHUNKS, int PASSES>
+hipError_t launch_rq(const uint16_t* X, const int32_t* perm, int rows, int K, uint8_t* Q, uint16_t* S,
+                     hipStream_t stream) {
+  const size_t lds = (size_t)K * sizeof(uint16_t);
+  static int per_cu = 0, cus = 0;                   // occupancy of this instantiation, filled on first use
+  if (per_cu == 0) {
+    int dev = 0, n = 0, b = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cus = n;
+    const size_t lds_max = (size_t)CHUNKS * 8 * kThreads * sizeof(uint16_t);   // largest row of this range
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, row_quantize_kernel<CHUNKS, PASSES>, kThreads, lds_max) ==
+            hipSuccess && b > 0)
+      per_cu = b;
+    if (cus <= 0) cus = 256;
+    if (per_cu <= 0) per_cu = 2;
+  }
+  const int lim = per_cu * cus;
+  const int grid = rows < lim ? rows : lim;         // persistent: one wave of workgroups
+  hipLaunchKernelGGL((row_quantize_kernel<CHUNKS, PASSES>), dim3(grid), dim3(kThreads), lds, stream, X, perm, rows,
+                     K, Q, S);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_row_quantize(const uint16_t* X, const int32_t* perm, int rows, int K, uint8_t* Q, uint16_t* S,
                                hipStream_t stream) {
-  const size_t lds = (size_t)K * sizeof(uint16_t);
-  hipLaunchKernelGGL(row_quantize_kernel, dim3(rows), dim3(kThreads), lds, stream, X, perm, rows, K, Q, S);
-  return hipGetLastError();
+  if (K <= 4096) return launch_rq<2, 1>(X, perm, rows, K, Q, S, stream);
+  if (K <= 8192) return launch_rq<4, 2>(X, perm, rows, K, Q, S, stream);
+  if (K <= 12288) return launch_rq<6, 3>(X, perm, rows, K, Q, S, stream);
+  if (K <= 16384) return launch_rq<8, 4>(X, perm, rows, K, Q, S, stream);
+  return launch_rq<ATOM_MAX_K / 8 / kThreads, 0>(X, perm, rows, K, Q, S, stream);
 }
 
 }  // namespace atom

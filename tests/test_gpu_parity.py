@@ -206,7 +206,7 @@ def test_gemm_llama70b_sampled():
 
 # --------------------------------------------------------------------------- ragged / edge shapes
 RAGGED = [(1, 1, 256), (2, 3, 256), (37, 200, 384), (130, 129, 1152), (257, 513, 640), (16, 512, 1024),
-          (128, 128, 256), (129, 255, 2048)]
+          (128, 128, 256), (129, 255, 2048), (33, 70, 12416), (20, 48, 16384), (9, 40, 20480)]
 
 
 @pytest.mark.parametrize("M,N,K", RAGGED)
