@@ -172,6 +172,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="resident input copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256, help="rows per shape in the CPU oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (steps times), to calibrate HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -187,8 +189,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
-    bq.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": max(1, args.steps)}), flush=True)
+        return
+    bq.load_library()
     keys = WORKLOAD_SETS[args.workload]
     R = max(1, args.rotate)
     if args.workload == "Dq":
