@@ -1,44 +1,44 @@
-// W4A4 grouped GEMM for gfx950 on int8 MFMA.
+// W4A4 grouped GEMM for gfx950 on the matrix cores.
 //
 // Y[m,n] = sum over 128-channel groups g of acc_g[m,n] * sx[g,m] * sw[g,n], with
 // acc_g = exact integer dot product of the codes of group g.  The method runs this product
 // on integer operators (index page of "Atom: Low-bit Quantization for Efficient and Accurate
-// LLM Serving", Abstract; quantization record, "notes": an integer-operator path).  gfx950
-// has no 4-bit MFMA, so the INT4 groups are widened to int8 in registers and fed to
-// v_mfma_i32_32x32x32_i8; the INT8 outlier group (record, "notes": a 128-channel
-// high-precision group) feeds the same instruction without widening.
+// LLM Serving", Abstract; quantization record, "notes": an integer-operator path, not FP4).
 //
-// Nibble widening.  For a packed word w holding codes c0..c7 (c_{2j} in the low nibble of
-// byte j), w & 0xF0F0F0F0 holds 16*c_{2j+1} and (w << 4) & 0xF0F0F0F0 holds 16*c_{2j} as
-// int8 bytes.  Both operands are widened the same way, so the MFMAs over the "low" words and
-// those over the "high" words together cover every channel of the group once, and the
-// accumulator holds 256 * acc_g exactly (|256*acc_g| <= 128*112*112 < 2^21, so its fp32
-// conversion is exact too).
+// INT4 groups.  gfx950 has no 4-bit integer MFMA.  An INT4 code q in [-7, 7] is exactly the
+// fp8 e4m3 subnormal with bits (q < 0) << 7 | |q| (value q * 2^-9), and the packed
+// sign-magnitude layout turns a 32-bit word of eight codes into four such bytes with one AND
+// (even codes: w & 0x87878787) or one rotate and one AND (odd codes: rotr(w, 4) & 0x87878787).
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit-exponent scales 2^9 * 2^9 then returns the
+// group's integer dot product exactly in fp32: every product and partial sum is an integer
+// of magnitude below 2^24.  The INT4 groups thus run at the dense fp8 rate (equal to the int8
+// rate) and their accumulators are already fp32.
+//
+// INT8 outlier group (record, "notes": a 128-channel high-precision group): int8 codes feed
+// v_mfma_i32_32x32x32_i8 directly; its int32 accumulators are converted once.
 //
 // Scales.  The rank-one product sx[g,:] (x) sw[g,:] of a 32x32 output tile comes from one
 // v_mfma_f32_32x32x8_f16 whose only nonzero K column/row holds the fp16 scales: fp16 x fp16
 // is exact in fp32, and the product lands in the accumulator layout.  The epilogue per output
-// element and group is then one int->fp32 conversion and one fp32 FMA.  The outlier group's
-// scale product is multiplied by 256 so that the whole sum carries the same factor 256, which
-// the final store removes (a power of two: exact).
+// element and group is then a single fp32 FMA.
 //
 // Pipeline.  A packed row is a sequence of 64-byte stages: stage s < G-1 is INT4 group s,
 // stages G-1 and G are the two 64-byte halves of the INT8 outlier group.  Each thread loads
 // its 16-byte chunks of a stage of the A (activation) and B (weight) tiles with buffer loads
-// (the stage offset is a scalar), widens them once, and writes the int8 operands to LDS
-// (double-buffered); every wave then reads ready-to-use MFMA operands.  The loads of stage
-// s+2 are in flight while stage s+1 is written to LDS and stage s is multiplied; one barrier
-// per stage.
+// (the stage offset is a scalar), decodes them once into fp8 bytes (INT8 stages are copied
+// as they are), and writes them to LDS (double-buffered); every wave then reads ready MFMA
+// operands.  The loads of stage s+2 are in flight while stage s+1 is written to LDS and stage
+// s is multiplied; one barrier per stage.
 //
-// LDS layout.  A staged row is 128 bytes = eight 16-byte chunks: chunk h*4 + q holds the
-// widened low (h = 0) or high (h = 1) nibbles of packed chunk q (the INT8 stages use chunks
-// 0..3 raw).  Chunk c of row r is stored at chunk position c ^ ((r >> 1) & 7), so the 16
-// lanes of a ds_read_b128 group (16 consecutive rows, same chunk) hit 16 different bank
-// groups.
+// LDS layout.  A staged row is 128 bytes = eight 16-byte chunks: chunk q (0..3) holds the
+// even-code bytes of packed chunk q, chunk 4 + q its odd-code bytes (INT8 stages use chunks
+// 0..3 raw).  Chunk c of row r is stored at position c ^ h((r >> 1) & 7), h a rotation of
+// three bits, so that the 16 lanes of a ds_read_b128 group (16 consecutive rows, one chunk)
+// and those of a ds_write_b128 group (4 rows x 4 chunks) each cover all 16 bank groups.
 //
 // Waves.  A workgroup of WAVES_M x WAVES_N waves computes a BM x BN tile of Y; each wave
-// owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile held as 32x32 MFMA tiles.  Lane l of a wave
-// supplies row (A) / column (B) l & 31 of a tile and K half l >> 5 of each chunk pair.
+// owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile held as 32x32 MFMA tiles.  Lane l supplies row
+// (A) / column (B) l & 31 of a tile and the K half l >> 5 of each operand.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
@@ -50,32 +50,40 @@ namespace {
 
 typedef int32_t v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int32_t v8i __attribute__((ext_vector_type(8)));
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // native vector: stays in VGPRs
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStageBytes = 64;          // bytes of one stage of a packed row
+constexpr int kLdsRow = 128;             // bytes of one staged (decoded) row in LDS
 constexpr int kXcds = 8;                 // accelerator complex dies (each with its own L2)
+constexpr int kScaleE8M0 = 127 + 9;      // 2^9: the e4m3 subnormal q * 2^-9 counts as q
 
-__device__ __forceinline__ v4i widen_lo(u32x4 p) {
-  return v4i{(int32_t)((p.x << 4) & 0xF0F0F0F0u), (int32_t)((p.y << 4) & 0xF0F0F0F0u),
-             (int32_t)((p.z << 4) & 0xF0F0F0F0u), (int32_t)((p.w << 4) & 0xF0F0F0F0u)};
+__device__ __forceinline__ uint32_t rotr4(uint32_t w) { return __builtin_amdgcn_alignbit(w, w, 4); }
+
+__device__ __forceinline__ u32x4 fp8_even(u32x4 w) { return w & 0x87878787u; }
+
+__device__ __forceinline__ u32x4 fp8_odd(u32x4 w) {
+  return u32x4{rotr4(w.x), rotr4(w.y), rotr4(w.z), rotr4(w.w)} & 0x87878787u;
 }
 
-__device__ __forceinline__ v4i widen_hi(u32x4 p) {
-  return v4i{(int32_t)(p.x & 0xF0F0F0F0u), (int32_t)(p.y & 0xF0F0F0F0u), (int32_t)(p.z & 0xF0F0F0F0u),
-             (int32_t)(p.w & 0xF0F0F0F0u)};
+__device__ __forceinline__ v16f mma_fp8(v8i a, v8i b, v16f c) {
+  // cbsz = blgp = 0: both operands fp8 e4m3; opsel 0 and E8M0 scale 2^9 on both sides
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kScaleE8M0, 0, kScaleE8M0);
 }
-
-__device__ __forceinline__ v4i as_v4i(u32x4 p) { return v4i{(int32_t)p.x, (int32_t)p.y, (int32_t)p.z, (int32_t)p.w}; }
 
 __device__ __forceinline__ v16i mma_i8(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ v16i mma_i8_first(v4i a, v4i b) {
-  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}, 0, 0, 0);
+// h: rotation of three bits, b2 b1 b0 -> b0 b2 b1
+__device__ __forceinline__ int chunk_swz(int row) {
+  const int k = (row >> 1) & 7;
+  return ((k & 1) << 2) | (k >> 1);
 }
+
+__device__ __forceinline__ int lds_pos(int row, int chunk) { return row * kLdsRow + ((chunk ^ chunk_swz(row)) << 4); }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 struct Tile {
@@ -91,8 +99,6 @@ struct Tile {
   static_assert(BM + BN <= kThreads, "one scale per thread per stage");
 };
 
-constexpr int kLdsRow = 128;             // bytes of one staged (widened) row in LDS
-
 // Registers holding one stage in flight between global memory and LDS.
 template <int APER, int BPER>
 struct StageRegs {
@@ -106,13 +112,11 @@ template <int APER, int BPER>
 struct StageAddr {
   __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc;  // the workgroup's rows of Xq / Wq
   int a_voff[APER], b_voff[BPER];          // byte offset of this thread's chunk in stage 0
-  int a_lds[APER], b_lds[BPER];            // LDS byte offset of the widened-low chunk
-  int a_lds_hi[APER], b_lds_hi[BPER];      // LDS byte offset of the widened-high chunk
+  int a_lds[APER], b_lds[BPER];            // LDS offset of chunk q (even codes, or the INT8 chunk)
+  int a_lds_odd[APER], b_lds_odd[BPER];    // LDS offset of chunk 4 + q (odd codes)
   const uint16_t* s_src;                   // this thread's scale column (or null)
   size_t s_stride;
 };
-
-__device__ __forceinline__ int swizzled(int row, int chunk) { return row * kLdsRow + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 template <int APER, int BPER>
 __device__ __forceinline__ void load_stage(StageRegs<APER, BPER>& st, const StageAddr<APER, BPER>& ad, int s, int G) {
@@ -126,24 +130,29 @@ __device__ __forceinline__ void load_stage(StageRegs<APER, BPER>& st, const Stag
   if (ad.s_src) st.s = ad.s_src[(size_t)min(s, G - 1) * ad.s_stride];
 }
 
-// INT4 stage: widen every chunk into its low- and high-nibble int8 chunks.
+template <int BM, int BN, bool kAcc>
+__device__ __forceinline__ void store_scale(uint16_t s, uint16_t* lsx, uint16_t* lsw, int tid) {
+  if (!kAcc) {
+    if (tid < BM) lsx[tid] = s;
+    else if (tid < BM + BN) lsw[tid - BM] = s;
+  }
+}
+
+// INT4 stage: decode every chunk into its even- and odd-code fp8 chunks.
 template <int BM, int BN, bool kAcc, int APER, int BPER>
 __device__ __forceinline__ void store_stage_int4(const StageRegs<APER, BPER>& st, const StageAddr<APER, BPER>& ad,
                                                  uint8_t* la, uint8_t* lb, uint16_t* lsx, uint16_t* lsw, int tid) {
 #pragma unroll
   for (int p = 0; p < APER; ++p) {
-    *reinterpret_cast<v4i*>(la + ad.a_lds[p]) = widen_lo(st.a[p]);
-    *reinterpret_cast<v4i*>(la + ad.a_lds_hi[p]) = widen_hi(st.a[p]);
+    *reinterpret_cast<u32x4*>(la + ad.a_lds[p]) = fp8_even(st.a[p]);
+    *reinterpret_cast<u32x4*>(la + ad.a_lds_odd[p]) = fp8_odd(st.a[p]);
   }
 #pragma unroll
   for (int p = 0; p < BPER; ++p) {
-    *reinterpret_cast<v4i*>(lb + ad.b_lds[p]) = widen_lo(st.b[p]);
-    *reinterpret_cast<v4i*>(lb + ad.b_lds_hi[p]) = widen_hi(st.b[p]);
+    *reinterpret_cast<u32x4*>(lb + ad.b_lds[p]) = fp8_even(st.b[p]);
+    *reinterpret_cast<u32x4*>(lb + ad.b_lds_odd[p]) = fp8_odd(st.b[p]);
   }
-  if (!kAcc) {
-    if (tid < BM) lsx[tid] = st.s;
-    else if (tid < BM + BN) lsw[tid - BM] = st.s;
-  }
+  store_scale<BM, BN, kAcc>(st.s, lsx, lsw, tid);
 }
 
 // INT8 stage: chunks are already int8 codes.
@@ -154,15 +163,12 @@ __device__ __forceinline__ void store_stage_int8(const StageRegs<APER, BPER>& st
   for (int p = 0; p < APER; ++p) *reinterpret_cast<u32x4*>(la + ad.a_lds[p]) = st.a[p];
 #pragma unroll
   for (int p = 0; p < BPER; ++p) *reinterpret_cast<u32x4*>(lb + ad.b_lds[p]) = st.b[p];
-  if (!kAcc) {
-    if (tid < BM) lsx[tid] = st.s;
-    else if (tid < BM + BN) lsw[tid - BM] = st.s;
-  }
+  store_scale<BM, BN, kAcc>(st.s, lsx, lsw, tid);
 }
 
 // kAcc = false: Y output.  kAcc = true: write the per-group integer accumulators instead.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool kAcc>
-__global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(4))) void gemm_w4a4_kernel(
+__global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx, const uint8_t* __restrict__ Wq,
     const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out) {
   using T = Tile<BM, BN, WAVES_M, WAVES_N>;
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   const int S = G + 1;                                  // stages per row
   const size_t rbytes = (size_t)S * kStageBytes;        // = (K-128)/2 + 128
   const int l32 = lane & 31;                            // row (A) / column (B) inside a 32x32 tile
-  const int kh = lane >> 5;                             // which 32-byte half of the stage this lane reads
+  const int kh = lane >> 5;                             // which K half of an operand this lane supplies
 
   // ---- per-thread staging addresses (rows past M / N repeat the last valid row)
   StageAddr<T::kAPer, T::kBPer> ad;
@@ -201,17 +207,17 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
                                                   (int)(rows_b * rbytes), 0x00020000);
 #pragma unroll
     for (int p = 0; p < T::kAPer; ++p) {
-      const int c = tid + p * T::kThreads, r = c / 4, q = c % 4;
-      ad.a_voff[p] = min(r, rows_a - 1) * (int)rbytes + q * 16;
-      ad.a_lds[p] = swizzled(r, q);
-      ad.a_lds_hi[p] = swizzled(r, 4 + q);
+      const int c = tid + p * T::kThreads, r = c / 4, qc = c % 4;
+      ad.a_voff[p] = min(r, rows_a - 1) * (int)rbytes + qc * 16;
+      ad.a_lds[p] = lds_pos(r, qc);
+      ad.a_lds_odd[p] = lds_pos(r, 4 + qc);
     }
 #pragma unroll
     for (int p = 0; p < T::kBPer; ++p) {
-      const int c = tid + p * T::kThreads, r = c / 4, q = c % 4;
-      ad.b_voff[p] = min(r, rows_b - 1) * (int)rbytes + q * 16;
-      ad.b_lds[p] = swizzled(r, q);
-      ad.b_lds_hi[p] = swizzled(r, 4 + q);
+      const int c = tid + p * T::kThreads, r = c / 4, qc = c % 4;
+      ad.b_voff[p] = min(r, rows_b - 1) * (int)rbytes + qc * 16;
+      ad.b_lds[p] = lds_pos(r, qc);
+      ad.b_lds_odd[p] = lds_pos(r, 4 + qc);
     }
     ad.s_src = nullptr;
     ad.s_stride = 0;
@@ -234,101 +240,61 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
     for (int j = 0; j < T::kTN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) yacc[i][j][r] = 0.0f;
-  v16i acc[T::kTM][T::kTN];
+  v16f accf[T::kTM][T::kTN];                            // group sums: exact integers in fp32
 
-  // This lane's 16-byte operand word of tile i (A) / j (B): chunk h*4 + kh*2 + w of its row.
-  // The swizzle term depends only on l32 (tile rows start at multiples of 32).
-  const int lane_swz = (l32 >> 1) & 7;
-  auto lds_a_word = [&](int buf, int i, int h, int w) {
-    return *reinterpret_cast<const v4i*>(lds_a[buf] + (wm * T::kWTM + i * 32 + l32) * kLdsRow +
-                                         (((h * 4 + kh * 2 + w) ^ lane_swz) << 4));
+  // 16-byte LDS chunk c of the row supplying this lane in tile i (A) / j (B).  The swizzle
+  // term depends only on l32 (tile rows start at multiples of 32).
+  const int lane_swz = chunk_swz(l32);
+  auto lds_a_chunk = [&](int buf, int i, int c) {
+    return *reinterpret_cast<const v4i*>(lds_a[buf] + (wm * T::kWTM + i * 32 + l32) * kLdsRow + ((c ^ lane_swz) << 4));
   };
-  auto lds_b_word = [&](int buf, int j, int h, int w) {
-    return *reinterpret_cast<const v4i*>(lds_b[buf] + (wn * T::kWTN + j * 32 + l32) * kLdsRow +
-                                         (((h * 4 + kh * 2 + w) ^ lane_swz) << 4));
+  auto lds_b_chunk = [&](int buf, int j, int c) {
+    return *reinterpret_cast<const v4i*>(lds_b[buf] + (wn * T::kWTN + j * 32 + l32) * kLdsRow + ((c ^ lane_swz) << 4));
+  };
+  // 32-byte fp8 operand of half h (0: even codes, 1: odd codes): chunks 4h + 2kh and 4h + 2kh + 1
+  auto fp8_a = [&](int buf, int i, int h) {
+    const v4i lo = lds_a_chunk(buf, i, 4 * h + 2 * kh), hi = lds_a_chunk(buf, i, 4 * h + 2 * kh + 1);
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  auto fp8_b = [&](int buf, int j, int h) {
+    const v4i lo = lds_b_chunk(buf, j, 4 * h + 2 * kh), hi = lds_b_chunk(buf, j, 4 * h + 2 * kh + 1);
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
 
-  // One INT4 group: four K=32 MFMAs per tile (widened low / high nibbles of two chunk words).
+  // One INT4 group: two K=64 fp8 MFMAs per tile (even codes, then odd codes).
   auto mma_int4 = [&](int buf) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
+      v8i bf[T::kTN];
 #pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        v4i af[T::kTM], bf[T::kTN];
+      for (int j = 0; j < T::kTN; ++j) bf[j] = fp8_b(buf, j, h);
 #pragma unroll
-        for (int i = 0; i < T::kTM; ++i) af[i] = lds_a_word(buf, i, h, w);
+      for (int i = 0; i < T::kTM; ++i) {
+        const v8i af = fp8_a(buf, i, h);
 #pragma unroll
-        for (int j = 0; j < T::kTN; ++j) bf[j] = lds_b_word(buf, j, h, w);
-#pragma unroll
-        for (int i = 0; i < T::kTM; ++i)
-#pragma unroll
-          for (int j = 0; j < T::kTN; ++j)
-            acc[i][j] = (h == 0 && w == 0) ? mma_i8_first(af[i], bf[j]) : mma_i8(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < T::kTN; ++j) accf[i][j] = mma_fp8(af, bf[j], h == 0 ? v16f{} : accf[i][j]);
       }
+    }
   };
 
-  // One 64-channel half of the INT8 outlier group: two K=32 MFMAs per tile.
-  auto mma_int8 = [&](int buf, bool first) {
+  // One 64-channel half of the INT8 outlier group: two K=32 int8 MFMAs per tile.
+  auto mma_int8_half = [&](int buf, bool first, v16i (&acc)[T::kTM][T::kTN]) {
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
-      v4i af[T::kTM], bf[T::kTN];
+      v4i bf[T::kTN];
 #pragma unroll
-      for (int i = 0; i < T::kTM; ++i) af[i] = lds_a_word(buf, i, 0, w);
+      for (int j = 0; j < T::kTN; ++j) bf[j] = lds_b_chunk(buf, j, 2 * kh + w);
 #pragma unroll
-      for (int j = 0; j < T::kTN; ++j) bf[j] = lds_b_word(buf, j, 0, w);
+      for (int i = 0; i < T::kTM; ++i) {
+        const v4i af = lds_a_chunk(buf, i, 2 * kh + w);
 #pragma unroll
-      for (int i = 0; i < T::kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::kTN; ++j)
-          acc[i][j] = (first && w == 0) ? mma_i8_first(af[i], bf[j]) : mma_i8(af[i], bf[j], acc[i][j]);
-    }
-  };
-
-  // Tile row i of an INT4 group (tiles (i, 0..kTN-1)): four K=32 MFMAs per tile.
-  auto mma_int4_row = [&](int buf, int i) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const v4i af = lds_a_word(buf, i, h, w);
-#pragma unroll
-        for (int j = 0; j < T::kTN; ++j) {
-          const v4i bf = lds_b_word(buf, j, h, w);
-          acc[i][j] = (h == 0 && w == 0) ? mma_i8_first(af, bf) : mma_i8(af, bf, acc[i][j]);
-        }
+        for (int j = 0; j < T::kTN; ++j) acc[i][j] = mma_i8(af, bf[j], (first && w == 0) ? v16i{} : acc[i][j]);
       }
-  };
-
-  // fp16 scale operands of one group for this lane: K column 0 of A holds sx (lanes < 32),
-  // K row 0 of B holds sw.
-  auto read_scales = [&](int buf, h4 (&sa)[T::kTM], h4 (&sb)[T::kTN]) {
-#pragma unroll
-    for (int i = 0; i < T::kTM; ++i) {
-      const uint16_t h = kh == 0 ? lds_sx[buf][wm * T::kWTM + i * 32 + l32] : (uint16_t)0;
-      sa[i] = h4{__builtin_bit_cast(_Float16, h), (_Float16)0, (_Float16)0, (_Float16)0};
-    }
-#pragma unroll
-    for (int j = 0; j < T::kTN; ++j) {
-      const uint16_t h = kh == 0 ? lds_sw[buf][wn * T::kWTN + j * 32 + l32] : (uint16_t)0;
-      sb[j] = h4{__builtin_bit_cast(_Float16, h), (_Float16)0, (_Float16)0, (_Float16)0};
     }
   };
 
-  // Epilogue of tile row i: yacc += float(acc) * (sx (x) sw); `outlier` scales the product by
-  // 256 so that every group's contribution carries the factor 256 of the widened groups.
-  auto epi_row = [&](int i, h4 sai, const h4 (&sb)[T::kTN], bool outlier) {
-#pragma unroll
-    for (int j = 0; j < T::kTN; ++j) {
-      v16f sp = __builtin_amdgcn_mfma_f32_32x32x8f16(sai, sb[j], v16f{}, 0, 0, 0);
-      if (outlier) sp *= 256.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) yacc[i][j][r] = __builtin_fmaf((float)acc[i][j][r], sp[r], yacc[i][j][r]);
-    }
-  };
-
-  // Scale the finished integer accumulators of group g into the fp32 output accumulators,
-  // or (kAcc) write them out.  `widened`: the accumulators carry the factor 256.
-  auto epilogue = [&](int buf, int g, bool widened) {
+  // Scale the group sums of group g (scales in LDS buffer buf) into yacc, or (kAcc) write them.
+  auto epilogue = [&](int buf, int g) {
     if (kAcc) {
 #pragma unroll
       for (int i = 0; i < T::kTM; ++i)
@@ -338,7 +304,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
           for (int r = 0; r < 16; ++r) {
             const int m = m0 + wm * T::kWTM + i * 32 + (r >> 2) * 8 + kh * 4 + (r & 3);
             const int n = n0 + wn * T::kWTN + j * 32 + l32;
-            if (m < M && n < N) acc_out[((size_t)g * M + m) * N + n] = widened ? (acc[i][j][r] >> 8) : acc[i][j][r];
+            if (m < M && n < N) acc_out[((size_t)g * M + m) * N + n] = (int32_t)accf[i][j][r];
           }
     } else {
       // rank-one scale operands: K column 0 of A holds sx, K row 0 of B holds sw (lanes < 32)
@@ -357,10 +323,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
       for (int i = 0; i < T::kTM; ++i)
 #pragma unroll
         for (int j = 0; j < T::kTN; ++j) {
-          v16f sp = __builtin_amdgcn_mfma_f32_32x32x8f16(sa[i], sb[j], v16f{}, 0, 0, 0);
-          if (!widened) sp *= 256.0f;
+          const v16f sp = __builtin_amdgcn_mfma_f32_32x32x8f16(sa[i], sb[j], v16f{}, 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) yacc[i][j][r] = __builtin_fmaf((float)acc[i][j][r], sp[r], yacc[i][j][r]);
+          for (int r = 0; r < 16; ++r) yacc[i][j][r] = __builtin_fmaf(accf[i][j][r], sp[r], yacc[i][j][r]);
         }
     }
   };
@@ -370,24 +335,34 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   load_stage(st, ad, 1, G);
   __syncthreads();
 
+  // INT4 groups: stages 0 .. G-2
+  for (int s = 0; s < G - 1; ++s) {
+    const int buf = s & 1;
+    mma_int4(buf);
+    // stage s+1 into the other buffer (released by the last barrier), then start stage s+2
+    if (s + 1 < G - 1)
+      store_stage_int4<BM, BN, kAcc>(st, ad, lds_a[buf ^ 1], lds_b[buf ^ 1], lds_sx[buf ^ 1], lds_sw[buf ^ 1], tid);
+    else
+      store_stage_int8<BM, BN, kAcc>(st, ad, lds_a[buf ^ 1], lds_b[buf ^ 1], lds_sx[buf ^ 1], lds_sw[buf ^ 1], tid);
+    load_stage(st, ad, s + 2, G);                    // s+2 <= G: always a valid stage
+    epilogue(buf, s);
+    __syncthreads();
+  }
+  // INT8 outlier group: stages G-1 and G
   {
-    for (int s = 0; s < G - 1; ++s) {
-      const int buf = s & 1;
-      mma_int4(buf);
-      if (s + 1 < G - 1)
-        store_stage_int4<BM, BN, kAcc>(st, ad, lds_a[buf ^ 1], lds_b[buf ^ 1], lds_sx[buf ^ 1], lds_sw[buf ^ 1], tid);
-      else
-        store_stage_int8<BM, BN, kAcc>(st, ad, lds_a[buf ^ 1], lds_b[buf ^ 1], lds_sx[buf ^ 1], lds_sw[buf ^ 1], tid);
-      load_stage(st, ad, s + 2, G);                  // s+2 <= G: always a valid stage
-      epilogue(buf, s, true);
-      __syncthreads();
-    }
+    v16i acc[T::kTM][T::kTN];
     const int buf = (G - 1) & 1;
-    mma_int8(buf, true);
+    mma_int8_half(buf, true, acc);
     store_stage_int8<BM, BN, kAcc>(st, ad, lds_a[buf ^ 1], lds_b[buf ^ 1], lds_sx[buf ^ 1], lds_sw[buf ^ 1], tid);
     __syncthreads();
-    mma_int8(buf ^ 1, false);
-    epilogue(buf ^ 1, G - 1, false);
+    mma_int8_half(buf ^ 1, false, acc);
+#pragma unroll
+    for (int i = 0; i < T::kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::kTN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accf[i][j][r] = (float)acc[i][j][r];   // |acc| <= 128*127*127 < 2^24
+    epilogue(buf ^ 1, G - 1);
   }
 
   if (!kAcc) {
@@ -399,14 +374,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm * T::kWTM + i * 32 + (r >> 2) * 8 + kh * 4 + (r & 3);
           const int n = n0 + wn * T::kWTN + j * 32 + l32;
-          if (m < M && n < N)
-            Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(yacc[i][j][r] * (1.0f / 256.0f)));
+          if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(yacc[i][j][r]));
         }
   }
 }
 
 // 128 x 128 workgroup tile, 2 x 2 waves of 64 x 64 (2 x 2 MFMA tiles of 32 x 32 each).
-constexpr int kBM = 128, kBN = 128, kWavesM = 2, kWavesN = 4;
+constexpr int kBM = 128, kBN = 128, kWavesM = 2, kWavesN = 2;
 
 }  // namespace
 

@@ -20,8 +20,13 @@
 // t = x*r, e = fma(-t, s, x), u = fma(e, r, t), the integer nearest u (ties to even) equals
 // the integer nearest the correctly rounded fp32 quotient x/s for every fp16 x and every
 // fp16 scale s this rule can produce (checked over all 2.0e9 such pairs on the CPU).
-// Adding 1.5*2^23 rounds the clamped value to that integer with ties to even and leaves its
-// two's-complement low byte in the low bits of the sum.
+// Adding 1.5*2^23 rounds the clamped value (or its magnitude) to that integer with ties to
+// even and leaves its two's-complement low byte in the low bits of the sum.
+//
+// Packed INT4 layout (sign-magnitude, chosen so that a GEMM can turn a word into fp8 e4m3
+// subnormals with one AND per parity): per 32-bit word of codes c0..c7, byte j holds |c_2j|
+// in bits 0-2, |c_2j+1| in bits 4-6, the sign of c_2j in bit 7 and the sign of c_2j-1 (byte
+// 0: of c7) in bit 3.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
@@ -50,14 +55,17 @@ __device__ __forceinline__ float group_max8(float a) {
   return a;
 }
 
-// Code of x for scale s (> 0) with reciprocal r, as the low byte of the returned word.
-__device__ __forceinline__ uint32_t code_bits(float x, float s, float r, float qmax) {
+// Clamped quotient of x for scale s (> 0) with reciprocal r; its nearest integer (ties to
+// even) is the code.
+__device__ __forceinline__ float code_value(float x, float s, float r, float qmax) {
   const float t = x * r;
   const float e = __builtin_fmaf(-t, s, x);
   const float u = __builtin_fmaf(e, r, t);
-  const float v = __builtin_amdgcn_fmed3f(u, -qmax, qmax);
-  return __float_as_uint(v + 12582912.0f);
+  return __builtin_amdgcn_fmed3f(u, -qmax, qmax);
 }
+
+// Adding 1.5 * 2^23 rounds to an integer (ties to even) and leaves it in the low bits.
+constexpr float kRound = 12582912.0f;
 
 // low bytes of a,b,c,d -> one word [a, b, c, d]
 __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -129,22 +137,37 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
     const float qmax = tail ? 127.0f : 7.0f;
     const __half s16 = __float2half_rn(a / qmax);      // correctly rounded fp32 divide, then RNE to fp16
     const float s = __half2float(s16);
-    uint32_t b[kPerThread];
+    float v[kPerThread];
     if (s > 0.0f) {
       const float r = 1.0f / s;
 #pragma unroll
-      for (int i = 0; i < kPerThread; ++i) b[i] = code_bits(x[i], s, r, qmax);
+      for (int i = 0; i < kPerThread; ++i) v[i] = code_value(x[i], s, r, qmax);
     } else {
 #pragma unroll
-      for (int i = 0; i < kPerThread; ++i) b[i] = 0;
+      for (int i = 0; i < kPerThread; ++i) v[i] = 0.0f;
     }
+    uint32_t b[kPerThread];                              // two's-complement code in the low byte
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) b[i] = __float_as_uint(v[i] + kRound);
     if (!tail) {
-      // nibbles: even codes in the low nibble of each byte, odd codes in the high nibble
+      // sign-magnitude INT4: per 32-bit word of codes c0..c7, byte j = |c_2j| | |c_2j+1| << 4 |
+      // sign(c_2j) << 7 | sign(c_2j-1) << 3 (byte 0 takes the sign of c7)
+      uint32_t m[kPerThread];                            // |code| in the low byte
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) m[i] = __float_as_uint(__builtin_fabsf(v[i]) + kRound);
       uint2 w;
-      const uint32_t e0 = pack4(b[0], b[2], b[4], b[6]), o0 = pack4(b[1], b[3], b[5], b[7]);
-      const uint32_t e1 = pack4(b[8], b[10], b[12], b[14]), o1 = pack4(b[9], b[11], b[13], b[15]);
-      w.x = (e0 & 0x0F0F0F0Fu) | ((o0 << 4) & 0xF0F0F0F0u);
-      w.y = (e1 & 0x0F0F0F0Fu) | ((o1 << 4) & 0xF0F0F0F0u);
+      uint32_t word[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int o = 8 * h;
+        const uint32_t ev = ((pack4(b[o], b[o + 2], b[o + 4], b[o + 6]) & 0x80808080u) |
+                             pack4(m[o], m[o + 2], m[o + 4], m[o + 6]));
+        const uint32_t od = (pack4(b[o + 1], b[o + 3], b[o + 5], b[o + 7]) & 0x80808080u) |
+                            pack4(m[o + 1], m[o + 3], m[o + 5], m[o + 7]);
+        word[h] = ev | ((od << 4) | (od >> 28));         // odd magnitudes to bits 4-6, odd signs to the next byte
+      }
+      w.x = word[0];
+      w.y = word[1];
       *reinterpret_cast<uint2*>(qrow + c / 2) = w;
     } else {
       u32x4 w;

@@ -20,9 +20,14 @@
  *   - Shapes: K is a multiple of 128 with 256 <= K <= ATOM_MAX_K; rows (M, N) >= 1 and
  *     <= ATOM_MAX_ROWS.  G = K/128 groups: groups 0..G-2 are INT4, group G-1 is the INT8
  *     outlier group.  RB = atom_row_bytes(K) = (K-128)/2 + 128 bytes per packed row.
- *   - Packed row format: byte j < (K-128)/2 holds reordered codes 2j (low nibble) and 2j+1
- *     (high nibble) as 4-bit two's complement in [-7, 7]; the last 128 bytes hold the INT8
- *     outlier codes in [-127, 127].  Scales are fp16, group-major [G, rows].
+ *   - Packed row format: the first (K-128)/2 bytes hold the K-128 reordered INT4 codes in
+ *     [-7, 7], sign-magnitude, in 32-bit little-endian words of eight consecutive codes
+ *     c0..c7.  Byte j (0..3) of a word holds |c_2j| in bits 0-2, the sign of c_2j in bit 7,
+ *     |c_2j+1| in bits 4-6, and in bit 3 the sign of c_2j-1 (byte 0: the sign of c7); a sign
+ *     bit is 1 exactly when its code is negative.  (w & 0x87878787 then gives the even codes
+ *     and rotr(w, 4) & 0x87878787 the odd codes as fp8 e4m3 values q * 2^-9.)  The last 128
+ *     bytes hold the INT8 outlier codes in [-127, 127], two's complement.  Scales are fp16,
+ *     group-major [G, rows].
  *   - Argument checks run on the host before any HIP call and return the status without
  *     enqueuing anything.  A failed launch returns ATOM_E_HIP.  Faults inside a kernel
  *     surface at the caller's next synchronization.  Calls that share no output buffer may

@@ -30,8 +30,9 @@ Readings taken where the pages are silent (each one is also a parameter of the H
 * scale: fp32 correctly rounded ``absmax / qmax``, rounded to nearest-even fp16 and stored
   fp16, group-major ``[G, rows]``; codes ``clamp(rint_even(fl32(x / s)))``; a zero scale
   gives zero codes;
-* packing: two's-complement nibbles, the even-indexed code in the low nibble; the 128
-  INT8 outlier codes are appended as the last 128 bytes of each row;
+* packing: INT4 codes in sign-magnitude form, two per byte, with each odd code's sign bit
+  rotated into the next byte of its 32-bit word (see ``pack_rows``); the 128 INT8 outlier
+  codes are appended as the last 128 two's-complement bytes of each row;
 * output: ``Y = sum_g acc_g * sx_g * sw_g`` rounded once to fp16 (round to nearest even).
 """
 from __future__ import annotations
@@ -128,15 +129,25 @@ def quantize_rows(X: np.ndarray, perm: np.ndarray):
 
 # --------------------------------------------------------------------------- step: pack / unpack
 def pack_rows(codes: np.ndarray) -> np.ndarray:
-    """int8 codes [rows, K] -> packed bytes [rows, (K-128)/2 + 128]."""
+    """int8 codes [rows, K] -> packed bytes [rows, (K-128)/2 + 128].
+
+    INT4 codes (the first K-128 reordered channels) are stored in sign-magnitude form, two
+    per byte, in 32-bit words of eight consecutive codes c0..c7.  Byte j of a word holds
+    |c_{2j}| in bits 0-2, the sign of c_{2j} in bit 7, |c_{2j+1}| in bits 4-6, and in bit 3 the
+    sign of the odd code c_{2j-1} of the previous byte (byte 0 holds the sign of c7).  The
+    sign bit is 1 exactly when the code is negative.  The 128 INT8 outlier codes follow as
+    two's-complement bytes."""
     codes = np.asarray(codes, dtype=np.int8)
     rows, K = codes.shape
     klo = K - OUTLIERS
-    u = codes.view(np.uint8)
-    lo = u[:, 0:klo:2] & 0x0F                  # even index -> low nibble
-    hi = u[:, 1:klo:2] & 0x0F                  # odd index  -> high nibble
-    body = (lo | (hi << 4)).astype(np.uint8)
-    tail = u[:, klo:]
+    q = codes[:, :klo].astype(np.int16).reshape(rows, klo // 8, 4, 2)     # [row, word, byte j, even/odd]
+    mag = np.abs(q).astype(np.uint8)
+    neg = (q < 0).astype(np.uint8)
+    even_m, odd_m = mag[..., 0], mag[..., 1]
+    even_s, odd_s = neg[..., 0], neg[..., 1]
+    odd_s_prev = np.roll(odd_s, 1, axis=2)                                 # byte j <- sign of byte j-1's odd code
+    body = (even_m | (odd_m << 4) | (even_s << 7) | (odd_s_prev << 3)).astype(np.uint8).reshape(rows, klo // 2)
+    tail = codes[:, klo:].view(np.uint8)
     return np.ascontiguousarray(np.concatenate([body, tail], axis=1))
 
 
@@ -147,14 +158,14 @@ def unpack_rows(packed: np.ndarray, K: int) -> np.ndarray:
     if packed.shape[1] != row_bytes(K):
         raise ValueError("packed row length does not match K")
     klo = K - OUTLIERS
-    body = packed[:, : klo // 2].astype(np.int16)
-    lo = body & 0x0F
-    hi = body >> 4
-    lo = np.where(lo >= 8, lo - 16, lo)
-    hi = np.where(hi >= 8, hi - 16, hi)
+    b = packed[:, : klo // 2].astype(np.int16).reshape(rows, klo // 8, 4)
+    even_m, odd_m = b & 7, (b >> 4) & 7
+    even_s = (b >> 7) & 1
+    odd_s = np.roll((b >> 3) & 1, -1, axis=2)                              # byte j's odd sign sits in byte j+1
+    even = np.where(even_s == 1, -even_m, even_m)
+    odd = np.where(odd_s == 1, -odd_m, odd_m)
     out = np.empty((rows, K), dtype=np.int8)
-    out[:, 0:klo:2] = lo
-    out[:, 1:klo:2] = hi
+    out[:, :klo] = np.stack([even, odd], axis=-1).reshape(rows, klo)
     out[:, klo:] = packed[:, klo // 2:].view(np.int8)
     return out
 
