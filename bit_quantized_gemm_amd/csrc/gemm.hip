@@ -18,23 +18,26 @@
 // v_mfma_i32_32x32x32_i8 directly; its int32 accumulators are converted once.
 //
 // Scales.  The rank-one product sx[g,:] (x) sw[g,:] of a 32x32 output tile comes from one
-// v_mfma_f32_32x32x8_f16 whose only nonzero K column/row holds the fp16 scales: fp16 x fp16
-// is exact in fp32, and the product lands in the accumulator layout.  The epilogue per output
-// element and group is then a single fp32 FMA.
+// v_mfma_f32_32x32x8_f16 whose only nonzero K slots (0 and 4) hold the fp16 scales: fp16 x
+// fp16 is exact in fp32, the two equal products sum exactly to 2 * sx * sw, and the result
+// lands in the accumulator layout.  The epilogue per output element and group is then a
+// single fp32 FMA; the factor 2 is removed once at the store.
 //
 // Pipeline.  A packed row is a sequence of 64-byte stages: stage s < G-1 is INT4 group s,
 // stages G-1 and G are the two 64-byte halves of the INT8 outlier group.  Each thread loads
 // its 16-byte chunks of a stage of the A (activation) and B (weight) tiles with buffer loads
-// (the stage offset is a scalar), decodes them once into fp8 bytes (INT8 stages are copied
-// as they are), and writes them to LDS (double-buffered); every wave then reads ready MFMA
-// operands.  The loads of stage s+2 are in flight while stage s+1 is written to LDS and stage
-// s is multiplied; one barrier per stage.
+// (the stage offset is a scalar) and copies them, still packed, to LDS (double-buffered).
+// Every wave reads the packed bytes of its own operands and decodes them in registers just
+// before the MFMAs that use them, so LDS carries 64 bytes per row and group (its write rate
+// is the scarce one) and the decode runs under the matrix core.  While group s is
+// multiplied, stage s+1 is written to LDS and the loads of stage s+2 are in flight; one
+// barrier per stage, placed before the last epilogues of group s so that the operand reads
+// of group s+1 overlap them.
 //
-// LDS layout.  A staged row is 128 bytes = eight 16-byte chunks: chunk q (0..3) holds the
-// even-code bytes of packed chunk q, chunk 4 + q its odd-code bytes (INT8 stages use chunks
-// 0..3 raw).  Chunk c of row r is stored at position c ^ h((r >> 1) & 7), h a rotation of
-// three bits, so that the 16 lanes of a ds_read_b128 group (16 consecutive rows, one chunk)
-// and those of a ds_write_b128 group (4 rows x 4 chunks) each cover all 16 bank groups.
+// LDS layout.  A staged row is 64 bytes = four 16-byte chunks; chunk c of row r is stored at
+// position c ^ ((r >> 2) & 3).  The 16 lanes of a ds_read_b128 group (16 consecutive rows,
+// one chunk) and those of a ds_write_b128 group (4 rows x 4 chunks) each cover all 16 bank
+// groups of 16 bytes.
 //
 // Waves.  A workgroup of WAVES_M x WAVES_N waves computes a BM x BN tile of Y; each wave
 // owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile held as 32x32 MFMA tiles.  Lane l supplies row
@@ -56,16 +59,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // native vector: 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStageBytes = 64;          // bytes of one stage of a packed row
-constexpr int kLdsRow = 128;             // bytes of one staged (decoded) row in LDS
+constexpr int kLdsRow = 64;              // bytes of one staged (packed) row in LDS
 constexpr int kXcds = 8;                 // accelerator complex dies (each with its own L2)
 constexpr int kScaleE8M0 = 127 + 9;      // 2^9: the e4m3 subnormal q * 2^-9 counts as q
 
 __device__ __forceinline__ uint32_t rotr4(uint32_t w) { return __builtin_amdgcn_alignbit(w, w, 4); }
 
-__device__ __forceinline__ u32x4 fp8_even(u32x4 w) { return w & 0x87878787u; }
+constexpr uint32_t kFp8Mask = 0x87878787u;   // sign bit and 3-bit magnitude of each byte
 
-__device__ __forceinline__ u32x4 fp8_odd(u32x4 w) {
-  return u32x4{rotr4(w.x), rotr4(w.y), rotr4(w.z), rotr4(w.w)} & 0x87878787u;
+// fp8 e4m3 operands of 32 packed INT4 codes pairs: even codes (w & mask) and odd codes
+// (rotr(w, 4) & mask) of each 32-bit word
+__device__ __forceinline__ v8i fp8_even(v8i w) { return w & (int)kFp8Mask; }
+
+__device__ __forceinline__ v8i fp8_odd(v8i w) {
+  v8i r;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r[k] = (int)(rotr4((uint32_t)w[k]) & kFp8Mask);
+  return r;
 }
 
 __device__ __forceinline__ v16f mma_fp8(v8i a, v8i b, v16f c) {
@@ -77,13 +87,9 @@ __device__ __forceinline__ v16i mma_i8(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
-// h: rotation of three bits, b2 b1 b0 -> b0 b2 b1
-__device__ __forceinline__ int chunk_swz(int row) {
-  const int k = (row >> 1) & 7;
-  return ((k & 1) << 2) | (k >> 1);
-}
+// Chunk position swizzle of LDS row r (rows are 64 bytes)
+__device__ __forceinline__ int chunk_swz(int r) { return (r >> 2) & 3; }
 
-__device__ __forceinline__ int lds_pos(int row, int chunk) { return row * kLdsRow + ((chunk ^ chunk_swz(row)) << 4); }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 struct Tile {
@@ -92,90 +98,63 @@ struct Tile {
   static constexpr int kWTN = BN / WAVES_N;            // wave tile columns
   static constexpr int kTM = kWTM / 32;                // MFMA tiles per wave (rows)
   static constexpr int kTN = kWTN / 32;                // MFMA tiles per wave (columns)
-  static constexpr int kAPer = BM * 4 / kThreads;      // 16-byte A chunks per thread per stage
-  static constexpr int kBPer = BN * 4 / kThreads;
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kDma = BM / kWaves / 16;        // LDS-DMA instructions per wave per stage and tile
   static_assert(kWTM % 32 == 0 && kWTN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(kAPer * kThreads == BM * 4 && kBPer * kThreads == BN * 4, "chunks must divide evenly");
-  static_assert(BM + BN <= kThreads, "one scale per thread per stage");
+  static_assert(BM + BN == kThreads, "one scale per thread per stage");
+  static_assert(BM == BN && kDma * kWaves * 16 == BM, "each wave copies whole 16-row slabs of A and B");
 };
 
-// Registers holding one stage in flight between global memory and LDS.
-template <int APER, int BPER>
-struct StageRegs {
-  u32x4 a[APER];
-  u32x4 b[BPER];
-  uint16_t s;
-};
-
-// Per-thread addressing of the global -> LDS copy, fixed for the whole K loop.
-template <int APER, int BPER>
+// Per-thread addressing of the stage copy, fixed for the whole K loop.  Wave w copies tile
+// rows [w * BM / W, (w + 1) * BM / W) of A and the same rows of B (W waves), 16 rows per
+// LDS-DMA instruction: lane i of instruction h lands at LDS row r = w * BM / W + 16h + i / 4,
+// position i % 4, so it loads chunk (i % 4) ^ chunk_swz(r) of that row.  Rows past M / N
+// repeat the last valid row.  Thread t < BM carries the activation scale of tile row t,
+// thread BM + u the weight scale of tile column u.
+template <int NDMA>
 struct StageAddr {
   __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc;  // the workgroup's rows of Xq / Wq
-  int a_voff[APER], b_voff[BPER];          // byte offset of this thread's chunk in stage 0
-  int a_lds[APER], b_lds[BPER];            // LDS offset of chunk q (even codes, or the INT8 chunk)
-  int a_lds_odd[APER], b_lds_odd[BPER];    // LDS offset of chunk 4 + q (odd codes)
-  const uint16_t* s_src;                   // this thread's scale column (or null)
-  size_t s_stride;
+  int a_voff[NDMA], b_voff[NDMA];          // byte offset of this lane's chunk in stage 0
+  int lds_row0;                            // first LDS row of this wave's copy (wave-uniform)
+  const uint16_t* s_src;                   // this thread's scale in group 0
+  bool s_is_x;                             // activation (stride M) or weight (stride N) scale
 };
 
-template <int APER, int BPER>
-__device__ __forceinline__ void load_stage(StageRegs<APER, BPER>& st, const StageAddr<APER, BPER>& ad, int s, int G) {
+// One LDS-DMA instruction: lane i loads 16 bytes at voff + soff of the buffer and writes them
+// to lds + 16 i (lds is wave-uniform).  Not a template: the LDS address-space cast exists
+// only for the device.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Copy stage s of this wave's rows into LDS (asynchronous; tracked by vmcnt).
+template <int NDMA>
+__device__ __forceinline__ void dma_stage(const StageAddr<NDMA>& ad, uint8_t* la, uint8_t* lb, int s) {
   const int soff = s * kStageBytes;
 #pragma unroll
-  for (int p = 0; p < APER; ++p)
-    st.a[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad.a_rsrc, ad.a_voff[p], soff, 0));
-#pragma unroll
-  for (int p = 0; p < BPER; ++p)
-    st.b[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad.b_rsrc, ad.b_voff[p], soff, 0));
-  if (ad.s_src) st.s = ad.s_src[(size_t)min(s, G - 1) * ad.s_stride];
-}
-
-template <int BM, int BN, bool kAcc>
-__device__ __forceinline__ void store_scale(uint16_t s, uint16_t* lsx, uint16_t* lsw, int tid) {
-  if (!kAcc) {
-    if (tid < BM) lsx[tid] = s;
-    else if (tid < BM + BN) lsw[tid - BM] = s;
+  for (int h = 0; h < NDMA; ++h) {
+    lds_dma16(ad.a_rsrc, la + (ad.lds_row0 + 16 * h) * kLdsRow, ad.a_voff[h], soff);
+    lds_dma16(ad.b_rsrc, lb + (ad.lds_row0 + 16 * h) * kLdsRow, ad.b_voff[h], soff);
   }
 }
 
-// INT4 stage: decode every chunk into its even- and odd-code fp8 chunks.
-template <int BM, int BN, bool kAcc, int APER, int BPER>
-__device__ __forceinline__ void store_stage_int4(const StageRegs<APER, BPER>& st, const StageAddr<APER, BPER>& ad,
-                                                 uint8_t* la, uint8_t* lb, uint16_t* lsx, uint16_t* lsw, int tid) {
-#pragma unroll
-  for (int p = 0; p < APER; ++p) {
-    *reinterpret_cast<u32x4*>(la + ad.a_lds[p]) = fp8_even(st.a[p]);
-    *reinterpret_cast<u32x4*>(la + ad.a_lds_odd[p]) = fp8_odd(st.a[p]);
-  }
-#pragma unroll
-  for (int p = 0; p < BPER; ++p) {
-    *reinterpret_cast<u32x4*>(lb + ad.b_lds[p]) = fp8_even(st.b[p]);
-    *reinterpret_cast<u32x4*>(lb + ad.b_lds_odd[p]) = fp8_odd(st.b[p]);
-  }
-  store_scale<BM, BN, kAcc>(st.s, lsx, lsw, tid);
-}
-
-// INT8 stage: chunks are already int8 codes.
-template <int BM, int BN, bool kAcc, int APER, int BPER>
-__device__ __forceinline__ void store_stage_int8(const StageRegs<APER, BPER>& st, const StageAddr<APER, BPER>& ad,
-                                                 uint8_t* la, uint8_t* lb, uint16_t* lsx, uint16_t* lsw, int tid) {
-#pragma unroll
-  for (int p = 0; p < APER; ++p) *reinterpret_cast<u32x4*>(la + ad.a_lds[p]) = st.a[p];
-#pragma unroll
-  for (int p = 0; p < BPER; ++p) *reinterpret_cast<u32x4*>(lb + ad.b_lds[p]) = st.b[p];
-  store_scale<BM, BN, kAcc>(st.s, lsx, lsw, tid);
+// This thread's scale of stage s (group min(s, G-1): the INT8 group fills two stages).
+template <int NDMA>
+__device__ __forceinline__ uint16_t load_scale(const StageAddr<NDMA>& ad, int s, int G, int M, int N) {
+  const int g = min(s, G - 1);
+  const size_t ox = (size_t)g * M, ow = (size_t)g * N;   // uniform
+  return ad.s_src[ad.s_is_x ? ox : ow];
 }
 
 // kAcc = false: Y output.  kAcc = true: write the per-group integer accumulators instead.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool kAcc>
-__global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a4_kernel(
+__global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(kAcc ? 1 : 2))) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx, const uint8_t* __restrict__ Wq,
     const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out) {
   using T = Tile<BM, BN, WAVES_M, WAVES_N>;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kLdsRow];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_sx[2][BM];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_sw[2][BN];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_s[2][BM + BN];   // sx of the tile rows, then sw
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -197,42 +176,25 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   const int l32 = lane & 31;                            // row (A) / column (B) inside a 32x32 tile
   const int kh = lane >> 5;                             // which K half of an operand this lane supplies
 
-  // ---- per-thread staging addresses (rows past M / N repeat the last valid row)
-  StageAddr<T::kAPer, T::kBPer> ad;
+  // ---- per-lane stage-copy addresses
+  StageAddr<T::kDma> ad;
   {
     const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
     ad.a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(Xq + (size_t)m0 * rbytes), (short)0,
                                                   (int)(rows_a * rbytes), 0x00020000);
     ad.b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(Wq + (size_t)n0 * rbytes), (short)0,
                                                   (int)(rows_b * rbytes), 0x00020000);
+    ad.lds_row0 = __builtin_amdgcn_readfirstlane(wave) * (BM / T::kWaves);
 #pragma unroll
-    for (int p = 0; p < T::kAPer; ++p) {
-      const int c = tid + p * T::kThreads, r = c / 4, qc = c % 4;
-      ad.a_voff[p] = min(r, rows_a - 1) * (int)rbytes + qc * 16;
-      ad.a_lds[p] = lds_pos(r, qc);
-      ad.a_lds_odd[p] = lds_pos(r, 4 + qc);
+    for (int h = 0; h < T::kDma; ++h) {
+      const int r = ad.lds_row0 + 16 * h + lane / 4, c = ((lane & 3) ^ chunk_swz(r)) * 16;
+      ad.a_voff[h] = min(r, rows_a - 1) * (int)rbytes + c;
+      ad.b_voff[h] = min(r, rows_b - 1) * (int)rbytes + c;
     }
-#pragma unroll
-    for (int p = 0; p < T::kBPer; ++p) {
-      const int c = tid + p * T::kThreads, r = c / 4, qc = c % 4;
-      ad.b_voff[p] = min(r, rows_b - 1) * (int)rbytes + qc * 16;
-      ad.b_lds[p] = lds_pos(r, qc);
-      ad.b_lds_odd[p] = lds_pos(r, 4 + qc);
-    }
-    ad.s_src = nullptr;
-    ad.s_stride = 0;
-    if (!kAcc) {
-      if (tid < BM) {
-        ad.s_src = sx + min(m0 + tid, M - 1);
-        ad.s_stride = (size_t)M;
-      } else if (tid < BM + BN) {
-        ad.s_src = sw + min(n0 + tid - BM, N - 1);
-        ad.s_stride = (size_t)N;
-      }
-    }
+    ad.s_is_x = tid < BM;
+    ad.s_src = kAcc ? nullptr : ad.s_is_x ? sx + min(m0 + tid, M - 1) : sw + min(n0 + tid - BM, N - 1);
   }
 
-  StageRegs<T::kAPer, T::kBPer> st;
   v16f yacc[T::kTM][T::kTN];
 #pragma unroll
   for (int i = 0; i < T::kTM; ++i)
@@ -240,129 +202,179 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
     for (int j = 0; j < T::kTN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) yacc[i][j][r] = 0.0f;
-  v16f accf[T::kTM][T::kTN];                            // group sums: exact integers in fp32
-
   // 16-byte LDS chunk c of the row supplying this lane in tile i (A) / j (B).  The swizzle
   // term depends only on l32 (tile rows start at multiples of 32).
   const int lane_swz = chunk_swz(l32);
+  const int a_row = (wm * T::kWTM + l32) * kLdsRow, b_row = (wn * T::kWTN + l32) * kLdsRow;
   auto lds_a_chunk = [&](int buf, int i, int c) {
-    return *reinterpret_cast<const v4i*>(lds_a[buf] + (wm * T::kWTM + i * 32 + l32) * kLdsRow + ((c ^ lane_swz) << 4));
+    return *reinterpret_cast<const v4i*>(lds_a[buf] + a_row + i * 32 * kLdsRow + ((c ^ lane_swz) << 4));
   };
   auto lds_b_chunk = [&](int buf, int j, int c) {
-    return *reinterpret_cast<const v4i*>(lds_b[buf] + (wn * T::kWTN + j * 32 + l32) * kLdsRow + ((c ^ lane_swz) << 4));
+    return *reinterpret_cast<const v4i*>(lds_b[buf] + b_row + j * 32 * kLdsRow + ((c ^ lane_swz) << 4));
   };
-  // 32-byte fp8 operand of half h (0: even codes, 1: odd codes): chunks 4h + 2kh and 4h + 2kh + 1
-  auto fp8_a = [&](int buf, int i, int h) {
-    const v4i lo = lds_a_chunk(buf, i, 4 * h + 2 * kh), hi = lds_a_chunk(buf, i, 4 * h + 2 * kh + 1);
-    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  };
-  auto fp8_b = [&](int buf, int j, int h) {
-    const v4i lo = lds_b_chunk(buf, j, 4 * h + 2 * kh), hi = lds_b_chunk(buf, j, 4 * h + 2 * kh + 1);
-    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  };
+  auto cat = [](v4i lo, v4i hi) { return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; };
 
-  // One INT4 group: two K=64 fp8 MFMAs per tile (even codes, then odd codes).
-  auto mma_int4 = [&](int buf) {
+  // Rank-one fp16 scale operands of a group: every lane puts its row's sx (A) / column's sw
+  // (B) in K slot 0 of its half, so the f16 MFMA returns 2 * sx * sw exactly (two equal
+  // exact products).  Every term of the Y accumulators thus carries the factor 2, which the
+  // final store removes; a power of two changes no rounding.
+  auto read_scales = [&](int buf, h4 (&sa)[T::kTM], h4 (&sb)[T::kTN]) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      v8i bf[T::kTN];
+    for (int i = 0; i < T::kTM; ++i) {
+      const uint16_t v = lds_s[buf][wm * T::kWTM + i * 32 + l32];
+      sa[i] = h4{__builtin_bit_cast(_Float16, v), (_Float16)0, (_Float16)0, (_Float16)0};
+    }
 #pragma unroll
-      for (int j = 0; j < T::kTN; ++j) bf[j] = fp8_b(buf, j, h);
-#pragma unroll
-      for (int i = 0; i < T::kTM; ++i) {
-        const v8i af = fp8_a(buf, i, h);
-#pragma unroll
-        for (int j = 0; j < T::kTN; ++j) accf[i][j] = mma_fp8(af, bf[j], h == 0 ? v16f{} : accf[i][j]);
-      }
+    for (int j = 0; j < T::kTN; ++j) {
+      const uint16_t v = lds_s[buf][BM + wn * T::kWTN + j * 32 + l32];
+      sb[j] = h4{__builtin_bit_cast(_Float16, v), (_Float16)0, (_Float16)0, (_Float16)0};
     }
   };
 
-  // One 64-channel half of the INT8 outlier group: two K=32 int8 MFMAs per tile.
-  auto mma_int8_half = [&](int buf, bool first, v16i (&acc)[T::kTM][T::kTN]) {
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      v4i bf[T::kTN];
-#pragma unroll
-      for (int j = 0; j < T::kTN; ++j) bf[j] = lds_b_chunk(buf, j, 2 * kh + w);
-#pragma unroll
-      for (int i = 0; i < T::kTM; ++i) {
-        const v4i af = lds_a_chunk(buf, i, 2 * kh + w);
-#pragma unroll
-        for (int j = 0; j < T::kTN; ++j) acc[i][j] = mma_i8(af, bf[j], (first && w == 0) ? v16i{} : acc[i][j]);
-      }
-    }
+  // Rank-one scale product 2 * sx (x) sw of tile (i, j), in the accumulator layout.
+  auto scale_product = [&](h4 sai, h4 sbj) {
+    return kAcc ? v16f{} : __builtin_amdgcn_mfma_f32_32x32x8f16(sai, sbj, v16f{}, 0, 0, 0);
   };
-
-  // Scale the group sums of group g (scales in LDS buffer buf) into yacc, or (kAcc) write them.
-  auto epilogue = [&](int buf, int g) {
+  // Group sum of tile (i, j) -> Y accumulators (or, kAcc, to acc_out for group g).
+  auto apply = [&](int i, int j, const v16f& acc, const v16f& sp, int g) {
     if (kAcc) {
 #pragma unroll
-      for (int i = 0; i < T::kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::kTN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = m0 + wm * T::kWTM + i * 32 + (r >> 2) * 8 + kh * 4 + (r & 3);
-            const int n = n0 + wn * T::kWTN + j * 32 + l32;
-            if (m < M && n < N) acc_out[((size_t)g * M + m) * N + n] = (int32_t)accf[i][j][r];
-          }
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * T::kWTM + i * 32 + (r >> 2) * 8 + kh * 4 + (r & 3);
+        const int n = n0 + wn * T::kWTN + j * 32 + l32;
+        if (m < M && n < N) acc_out[((size_t)g * M + m) * N + n] = (int32_t)acc[r];   // exact integers
+      }
     } else {
-      // rank-one scale operands: K column 0 of A holds sx, K row 0 of B holds sw (lanes < 32)
-      h4 sa[T::kTM], sb[T::kTN];
 #pragma unroll
-      for (int i = 0; i < T::kTM; ++i) {
-        const uint16_t h = kh == 0 ? lds_sx[buf][wm * T::kWTM + i * 32 + l32] : (uint16_t)0;
-        sa[i] = h4{__builtin_bit_cast(_Float16, h), (_Float16)0, (_Float16)0, (_Float16)0};
-      }
-#pragma unroll
-      for (int j = 0; j < T::kTN; ++j) {
-        const uint16_t h = kh == 0 ? lds_sw[buf][wn * T::kWTN + j * 32 + l32] : (uint16_t)0;
-        sb[j] = h4{__builtin_bit_cast(_Float16, h), (_Float16)0, (_Float16)0, (_Float16)0};
-      }
-#pragma unroll
-      for (int i = 0; i < T::kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::kTN; ++j) {
-          const v16f sp = __builtin_amdgcn_mfma_f32_32x32x8f16(sa[i], sb[j], v16f{}, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) yacc[i][j][r] = __builtin_fmaf(accf[i][j][r], sp[r], yacc[i][j][r]);
-        }
+      for (int r = 0; r < 16; ++r) yacc[i][j][r] = __builtin_fmaf(acc[r], sp[r], yacc[i][j][r]);
     }
   };
+  auto finish_tile = [&](int i, int j, const v16f& acc, h4 sai, h4 sbj, int g) {
+    apply(i, j, acc, scale_product(sai, sbj), g);
+  };
 
-  load_stage(st, ad, 0, G);
-  store_stage_int4<BM, BN, kAcc>(st, ad, lds_a[0], lds_b[0], lds_sx[0], lds_sw[0], tid);   // G >= 2: stage 0 is INT4
-  load_stage(st, ad, 1, G);
-  __syncthreads();
+  // This wave's packed operand bytes of one stage: for tile row i (A) / column j (B), the
+  // lane's row, chunks 2kh and 2kh+1 (stage bytes 32kh .. 32kh+31).  On an INT4 stage these
+  // are 64 codes whose even and odd halves are the lane's K=32 slices of the two K=64 fp8
+  // operands; on an INT8 stage, its K slices of two K=32 int8 operands.
+  auto read_packed = [&](int buf, v8i (&pa)[T::kTM], v8i (&pb)[T::kTN]) {
+#pragma unroll
+    for (int i = 0; i < T::kTM; ++i) pa[i] = cat(lds_a_chunk(buf, i, 2 * kh), lds_a_chunk(buf, i, 2 * kh + 1));
+#pragma unroll
+    for (int j = 0; j < T::kTN; ++j) pb[j] = cat(lds_b_chunk(buf, j, 2 * kh), lds_b_chunk(buf, j, 2 * kh + 1));
+  };
 
-  // INT4 groups: stages 0 .. G-2
-  for (int s = 0; s < G - 1; ++s) {
-    const int buf = s & 1;
-    mma_int4(buf);
-    // stage s+1 into the other buffer (released by the last barrier), then start stage s+2
-    if (s + 1 < G - 1)
-      store_stage_int4<BM, BN, kAcc>(st, ad, lds_a[buf ^ 1], lds_b[buf ^ 1], lds_sx[buf ^ 1], lds_sw[buf ^ 1], tid);
-    else
-      store_stage_int8<BM, BN, kAcc>(st, ad, lds_a[buf ^ 1], lds_b[buf ^ 1], lds_sx[buf ^ 1], lds_sw[buf ^ 1], tid);
-    load_stage(st, ad, s + 2, G);                    // s+2 <= G: always a valid stage
-    epilogue(buf, s);
-    __syncthreads();
+  // Stage s+1 (packed codes by LDS DMA, scales through a register loaded one stage earlier)
+  // is written during group s; `sreg` holds the scale of the next stage to write.
+  uint16_t sreg = 0;
+  if (!kAcc) sreg = load_scale(ad, 0, G, M, N);
+  dma_stage(ad, lds_a[0], lds_b[0], 0);
+  if (!kAcc) {
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_s[0][tid] = sreg;
+    sreg = load_scale(ad, 1, G, M, N);
   }
-  // INT8 outlier group: stages G-1 and G
-  {
-    v16i acc[T::kTM][T::kTN];
-    const int buf = (G - 1) & 1;
-    mma_int8_half(buf, true, acc);
-    store_stage_int8<BM, BN, kAcc>(st, ad, lds_a[buf ^ 1], lds_b[buf ^ 1], lds_sx[buf ^ 1], lds_sw[buf ^ 1], tid);
+  __builtin_amdgcn_s_waitcnt(0);                    // this wave's copies have landed
+  __syncthreads();
+  // stage 1 into buffer 1 (nobody reads it before the first barrier of the loop)
+  if (!kAcc) {
+    lds_s[1][tid] = sreg;
+    sreg = load_scale(ad, 2, G, M, N);
+  }
+  dma_stage(ad, lds_a[1], lds_b[1], 1);
+  v8i pa[T::kTM], pb[T::kTN];
+  h4 sa[T::kTM], sb[T::kTN];
+  if (!kAcc) read_scales(0, sa, sb);
+  read_packed(0, pa, pb);
+
+  // INT4 groups s = 0 .. G-2, packed operands of group s already in registers.  A wave
+  // issues in order, so nothing may wait on the MFMA issued just before it.  Per tile row i:
+  // region a decodes A row i (and every B column at i = 0), applies tile (i-1, 0), issues
+  // the scale product of tile (i, 0) and the even-code MFMAs of tiles (i, 0) and (i, 1);
+  // region b applies tile (i-1, 1), issues the scale product of tile (i, 1) and the odd-code
+  // MFMAs of both tiles, each after an independent MFMA.  A tile's sums (two K=64 fp8 MFMAs:
+  // the exact group sum in fp32) and its scale product are complete when the next tile row
+  // applies them.  The scheduling fences keep this order.  The barrier at the end publishes
+  // stage s+1 (copied during the previous iteration); its operands are read right after it,
+  // then stage s+2 is copied into the buffer stage s came from, and the last tile row is
+  // applied meanwhile.
+  static_assert(T::kTN == 2, "tile rows are processed as pairs of 32x32 tiles");
+  auto int4_group = [&](int s) {
+    const int buf = s & 1;
+    v16f acc[T::kTM][2], sp[T::kTM][2];
+    v8i be[2], bo[2];
+#pragma unroll
+    for (int i = 0; i < T::kTM; ++i) {
+      const v8i ae = fp8_even(pa[i]), ao = fp8_odd(pa[i]);
+      if (i == 0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          be[j] = fp8_even(pb[j]);
+          bo[j] = fp8_odd(pb[j]);
+        }
+      }
+      if (i > 0) apply(i - 1, 0, acc[i - 1][0], sp[i - 1][0], s);
+      sp[i][0] = scale_product(sa[i], sb[0]);
+      acc[i][0] = mma_fp8(ae, be[0], v16f{});
+      acc[i][1] = mma_fp8(ae, be[1], v16f{});
+      __builtin_amdgcn_sched_barrier(0);
+      if (i > 0) apply(i - 1, 1, acc[i - 1][1], sp[i - 1][1], s);
+      sp[i][1] = scale_product(sa[i], sb[1]);
+      acc[i][0] = mma_fp8(ao, bo[0], acc[i][0]);
+      acc[i][1] = mma_fp8(ao, bo[1], acc[i][1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    apply(T::kTM - 1, 0, acc[T::kTM - 1][0], sp[T::kTM - 1][0], s);
+    h4 san[T::kTM], sbn[T::kTN];
+    __builtin_amdgcn_s_waitcnt(0);                  // this wave's copies of stage s+1 have landed
     __syncthreads();
-    mma_int8_half(buf ^ 1, false, acc);
+    if (!kAcc) read_scales(buf ^ 1, san, sbn);       // first: LDS returns in order
+    read_packed(buf ^ 1, pa, pb);                    // group s+1 (INT8 half 0 when s = G-2)
+    // stage s+2 into buffer `buf`: its operands were read before this barrier; issued after
+    // the reads so that they need not wait for it, and the scale load first so that waiting
+    // for the copy covers it
+    if (!kAcc) {
+      lds_s[buf][tid] = sreg;
+      sreg = load_scale(ad, s + 3, G, M, N);
+    }
+    dma_stage(ad, lds_a[buf], lds_b[buf], s + 2);    // s <= G-2: a valid stage
+    apply(T::kTM - 1, 1, acc[T::kTM - 1][1], sp[T::kTM - 1][1], s);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < T::kTM; ++i) sa[i] = san[i];
+#pragma unroll
+    for (int j = 0; j < T::kTN; ++j) sb[j] = sbn[j];
+  };
+  for (int s = 0; s < G - 1; ++s) int4_group(s);
+
+  // INT8 outlier group: stage G-1 (its packed operands are in pa / pb) and stage G (copied by
+  // the last iteration), each two K=32 int8 MFMAs per tile; sa / sb hold the group's scales.
+  {
+    const int buf = G & 1;
+    v16i acc[T::kTM][T::kTN];
+    auto lo = [](v8i v) { return v4i{v[0], v[1], v[2], v[3]}; };
+    auto hi = [](v8i v) { return v4i{v[4], v[5], v[6], v[7]}; };
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i)
 #pragma unroll
-      for (int j = 0; j < T::kTN; ++j)
+      for (int j = 0; j < T::kTN; ++j) {
+        acc[i][j] = mma_i8(lo(pa[i]), lo(pb[j]), v16i{});
+        acc[i][j] = mma_i8(hi(pa[i]), hi(pb[j]), acc[i][j]);
+      }
+    __builtin_amdgcn_s_waitcnt(0);                  // stage G, copied by the last iteration
+    __syncthreads();
+    read_packed(buf, pa, pb);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) accf[i][j][r] = (float)acc[i][j][r];   // |acc| <= 128*127*127 < 2^24
-    epilogue(buf ^ 1, G - 1);
+    for (int i = 0; i < T::kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::kTN; ++j) {
+        acc[i][j] = mma_i8(lo(pa[i]), lo(pb[j]), acc[i][j]);
+        acc[i][j] = mma_i8(hi(pa[i]), hi(pb[j]), acc[i][j]);
+        v16f accf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accf[r] = (float)acc[i][j][r];   // |acc| <= 128*127*127 < 2^24: exact
+        finish_tile(i, j, accf, sa[i], sb[j], G - 1);
+      }
   }
 
   if (!kAcc) {
@@ -374,7 +386,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm * T::kWTM + i * 32 + (r >> 2) * 8 + kh * 4 + (r & 3);
           const int n = n0 + wn * T::kWTN + j * 32 + l32;
-          if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(yacc[i][j][r]));
+          if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][r]));
         }
   }
 }
