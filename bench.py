@@ -5,9 +5,10 @@ Llama-7B linear-layer shapes, as a fraction of the dense INT8 MFMA peak.
 
 One step = for each Llama-7B shape (attention projection 256x4096x4096, MLP gate/up
 1024x4096x11008, MLP down 2048x11008x4096): atom_quantize_act on a fresh fp16 activation
-batch, then atom_gemm against pre-packed weights.  Outlier selection and weight packing are
-offline steps of the method and run once before timing.  Effective TOPS = sum of 2*M*N*K
-over the shapes / step time.  Inputs rotate over several resident copies so that each step
+batch, then the grouped GEMM against pre-packed weights (atom_gemm_ws: shapes with few
+output tiles split their groups over several workgroups through a preallocated workspace).
+Outlier selection and weight packing are offline steps of the method and run once before
+timing.  Effective TOPS = sum of 2*M*N*K over the shapes / step time.  Inputs rotate over several resident copies so that each step
 reads its activations and packed weights from HBM rather than from the 256 MB Infinity
 Cache.
 
@@ -223,7 +224,10 @@ def main():
                                Xq=torch.empty((w.M, bq.atom_row_bytes(w.K)), dtype=torch.uint8, device=dev),
                                sx=torch.empty((w.K // 128, w.M), dtype=torch.float16, device=dev),
                                Y=torch.empty((w.M, w.N), dtype=torch.float16, device=dev)))
-        sets.append(dict(key=key, w=w, perm=perm, copies=copies))
+        # split-K scratch for shapes with few output tiles (allocated once, outside the timed region)
+        need = bq.atom_gemm_workspace_bytes(w.M, w.N, w.K)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        sets.append(dict(key=key, w=w, perm=perm, copies=copies, ws=ws))
         log(f"[setup] {key} {w.name} ready ({R} copies)")
     torch.cuda.synchronize()
 
@@ -238,7 +242,7 @@ def main():
             bq.atom_quantize_act(c["X"], s["perm"], Xq=c["Xq"], sx=c["sx"], stream=stream)
             if evs is not None:
                 evs[si][1].record(stream)
-            bq.atom_gemm(c["Xq"], c["sx"], c["Wq"], c["sw"], w.K, Y=c["Y"], stream=stream)
+            bq.atom_gemm_ws(c["Xq"], c["sx"], c["Wq"], c["sw"], w.K, s["ws"], Y=c["Y"], stream=stream)
             if evs is not None:
                 evs[si][2].record(stream)
 

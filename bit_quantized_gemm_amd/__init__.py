@@ -23,7 +23,8 @@ import os
 __all__ = [
     "AtomError", "EXPORTS", "GROUP", "OUTLIERS", "MAX_K", "lib_path", "load_library",
     "atom_row_bytes", "atom_num_groups", "atom_strerror", "atom_channel_stat", "atom_select_outliers",
-    "atom_pack_weights", "atom_quantize_act", "atom_gemm", "atom_gemm_group_acc", "linear",
+    "atom_pack_weights", "atom_quantize_act", "atom_gemm", "atom_gemm_workspace_bytes", "atom_gemm_ws",
+    "atom_gemm_group_acc", "linear",
 ]
 
 GROUP = 128
@@ -33,7 +34,8 @@ MAX_K = 32768
 # Every symbol declared in include/atom.h.
 EXPORTS = (
     "atom_row_bytes", "atom_num_groups", "atom_strerror", "atom_channel_stat", "atom_select_outliers",
-    "atom_pack_weights", "atom_quantize_act", "atom_gemm", "atom_gemm_group_acc",
+    "atom_pack_weights", "atom_quantize_act", "atom_gemm", "atom_gemm_workspace_bytes", "atom_gemm_ws",
+    "atom_gemm_group_acc",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +69,8 @@ def load_library():
         "atom_pack_weights": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp]),
         "atom_quantize_act": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp]),
         "atom_gemm": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp]),
+        "atom_gemm_workspace_bytes": (i64, [i32, i32, i32]),
+        "atom_gemm_ws": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp, i64, vp]),
         "atom_gemm_group_acc": (ctypes.c_int, [vp, vp, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -194,6 +198,31 @@ def atom_gemm(Xq, sx, Wq, sw, K, Y=None, stream=None):
     return Y
 
 
+def atom_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    r = load_library().atom_gemm_workspace_bytes(M, N, K)
+    if r < 0:
+        raise AtomError(f"atom_gemm_workspace_bytes: {atom_strerror(-r)}")
+    return r
+
+
+def atom_gemm_ws(Xq, sx, Wq, sw, K, workspace, Y=None, stream=None):
+    """atom_gemm with a caller-allocated workspace (uint8 tensor on the same device, or None)."""
+    torch = _torch()
+    M = Xq.shape[0]
+    N = Wq.shape[0]
+    if Y is None:
+        Y = _empty((M, N), torch.float16, Xq)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace", torch.uint8)
+        ws_bytes = workspace.numel()
+    st = load_library().atom_gemm_ws(_dev(Xq, "Xq", torch.uint8), _dev(sx, "sx", torch.float16),
+                                     _dev(Wq, "Wq", torch.uint8), _dev(sw, "sw", torch.float16), M, N, K,
+                                     _dev(Y, "Y", torch.float16), ws_ptr, ws_bytes, _stream(stream, Xq.device))
+    _check(st, "atom_gemm_ws")
+    return Y
+
+
 def atom_gemm_group_acc(Xq, Wq, K, acc=None, stream=None):
     torch = _torch()
     M = Xq.shape[0]
@@ -206,7 +235,13 @@ def atom_gemm_group_acc(Xq, Wq, K, acc=None, stream=None):
     return acc
 
 
-def linear(X, perm, Wq, sw, Y=None, stream=None):
-    """Runtime forward of the layer: quantize X, then the grouped GEMM (two launches, one stream)."""
+def linear(X, perm, Wq, sw, Y=None, stream=None, workspace=None):
+    """Runtime forward of the layer: quantize X, then the grouped GEMM (one stream).  The GEMM
+    uses split-K scratch when the shape needs it: `workspace` if given, else a torch buffer."""
+    torch = _torch()
     Xq, sx = atom_quantize_act(X, perm, stream=stream)
-    return atom_gemm(Xq, sx, Wq, sw, X.shape[1], Y=Y, stream=stream)
+    K = X.shape[1]
+    need = atom_gemm_workspace_bytes(X.shape[0], Wq.shape[0], K)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    return atom_gemm_ws(Xq, sx, Wq, sw, K, workspace if need else None, Y=Y, stream=stream)

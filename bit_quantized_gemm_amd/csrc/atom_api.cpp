@@ -109,20 +109,36 @@ int atom_quantize_act(const void* X, const int32_t* perm, int32_t M, int32_t K, 
                                               static_cast<hipStream_t>(stream)));
 }
 
-int atom_gemm(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N, int32_t K, void* Y,
-              void* stream) {
+int64_t atom_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return -(int64_t)ATOM_E_SHAPE;
+  const int splits = atom::gemm_splits(M, N, K);
+  return splits > 1 ? (int64_t)splits * M * N * 4 : 0;
+}
+
+int atom_gemm_ws(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N, int32_t K,
+                 void* Y, void* workspace, int64_t workspace_bytes, void* stream) {
   if (!Xq || !sx || !Wq || !sw || !Y) return ATOM_E_NULL;
   if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return ATOM_E_SHAPE;
   if (!aligned16(Xq) || !aligned16(sx) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y)) return ATOM_E_ALIGN;
+  int splits = atom::gemm_splits(M, N, K);
+  const int64_t need = splits > 1 ? (int64_t)splits * M * N * 4 : 0;
+  if (!workspace || workspace_bytes < need) splits = 1;   // too little scratch: one workgroup per tile
+  if (splits > 1 && !aligned16(workspace)) return ATOM_E_ALIGN;
   const uint64_t G = (uint64_t)K / ATOM_GROUP;
   const uint64_t rb = (uint64_t)atom_row_bytes(K);
   const Range in[4] = {range_of(Xq, (uint64_t)M * rb), range_of(sx, G * M * 2), range_of(Wq, (uint64_t)N * rb),
                        range_of(sw, G * N * 2)};
-  const Range out[1] = {range_of(Y, (uint64_t)M * N * 2)};
-  if (int s = check_overlap(in, 4, out, 1)) return s;
+  const Range out[2] = {range_of(Y, (uint64_t)M * N * 2), range_of(workspace, splits > 1 ? (uint64_t)need : 0)};
+  if (int s = check_overlap(in, 4, out, splits > 1 ? 2 : 1)) return s;
   return hip_status(atom::launch_gemm(static_cast<const uint8_t*>(Xq), static_cast<const uint16_t*>(sx),
                                       static_cast<const uint8_t*>(Wq), static_cast<const uint16_t*>(sw), M, N, K,
-                                      static_cast<uint16_t*>(Y), static_cast<hipStream_t>(stream)));
+                                      static_cast<uint16_t*>(Y), static_cast<float*>(workspace), splits,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int atom_gemm(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N, int32_t K, void* Y,
+              void* stream) {
+  return atom_gemm_ws(Xq, sx, Wq, sw, M, N, K, Y, nullptr, 0, stream);
 }
 
 int atom_gemm_group_acc(const void* Xq, const void* Wq, int32_t M, int32_t N, int32_t K, int32_t* acc,

@@ -147,10 +147,14 @@ __device__ __forceinline__ uint16_t load_scale(const StageAddr<NDMA>& ad, int s,
 }
 
 // kAcc = false: Y output.  kAcc = true: write the per-group integer accumulators instead.
+// splits > 1 (Y output only): the INT4 groups of a tile are divided among `splits`
+// workgroups (the last one also takes the INT8 group), each writing its fp32 sum, still
+// carrying the factor 2 of the scale products, to part[split][m][n].
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool kAcc>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(kAcc ? 1 : 2))) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx, const uint8_t* __restrict__ Wq,
-    const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out) {
+    const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out,
+    int splits, float* __restrict__ part) {
   using T = Tile<BM, BN, WAVES_M, WAVES_N>;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kLdsRow];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * kLdsRow];
@@ -165,12 +169,17 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   // XCD gets a contiguous run of tiles, M fastest, so an XCD's L2 holds one slice of W.
   const int tiles_m = (M + BM - 1) / BM;
   const int ntiles = tiles_m * ((N + BN - 1) / BN);
+  const int nblocks = ntiles * splits;
   const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
-  const int q = ntiles / kXcds, rem = ntiles % kXcds;
-  const int lin = xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+  const int q = nblocks / kXcds, rem = nblocks % kXcds;
+  const int lin2 = xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+  const int lin = lin2 % ntiles, split = lin2 / ntiles;
   const int m0 = (lin % tiles_m) * BM;
   const int n0 = (lin / tiles_m) * BN;
   const int G = K / ATOM_GROUP;
+  // this workgroup's INT4 groups [ga, gb); the last split also takes the INT8 group
+  const int ga = split * (G - 1) / splits, gb = (split + 1) * (G - 1) / splits;
+  const bool last_split = split == splits - 1;
   const int S = G + 1;                                  // stages per row
   const size_t rbytes = (size_t)S * kStageBytes;        // = (K-128)/2 + 128
   const int l32 = lane & 31;                            // row (A) / column (B) inside a 32x32 tile
@@ -267,21 +276,21 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   // Stage s+1 (packed codes by LDS DMA, scales through a register loaded one stage earlier)
   // is written during group s; `sreg` holds the scale of the next stage to write.
   uint16_t sreg = 0;
-  if (!kAcc) sreg = load_scale(ad, 0, G, M, N);
-  dma_stage(ad, lds_a[0], lds_b[0], 0);
+  if (!kAcc) sreg = load_scale(ad, ga, G, M, N);
+  dma_stage(ad, lds_a[0], lds_b[0], ga);
   if (!kAcc) {
     __builtin_amdgcn_s_waitcnt(0);
     lds_s[0][tid] = sreg;
-    sreg = load_scale(ad, 1, G, M, N);
+    sreg = load_scale(ad, ga + 1, G, M, N);
   }
   __builtin_amdgcn_s_waitcnt(0);                    // this wave's copies have landed
   __syncthreads();
   // stage 1 into buffer 1 (nobody reads it before the first barrier of the loop)
   if (!kAcc) {
     lds_s[1][tid] = sreg;
-    sreg = load_scale(ad, 2, G, M, N);
+    sreg = load_scale(ad, ga + 2, G, M, N);
   }
-  dma_stage(ad, lds_a[1], lds_b[1], 1);
+  dma_stage(ad, lds_a[1], lds_b[1], ga + 1);         // ga + 1 <= G
   v8i pa[T::kTM], pb[T::kTN];
   h4 sa[T::kTM], sb[T::kTN];
   if (!kAcc) read_scales(0, sa, sb);
@@ -300,7 +309,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   // applied meanwhile.
   static_assert(T::kTN == 2, "tile rows are processed as pairs of 32x32 tiles");
   auto int4_group = [&](int s) {
-    const int buf = s & 1;
+    const int buf = (s - ga) & 1;                    // stage s lives in buffer (s - ga) % 2
     v16f acc[T::kTM][2], sp[T::kTM][2];
     v8i be[2], bo[2];
 #pragma unroll
@@ -337,7 +346,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
       lds_s[buf][tid] = sreg;
       sreg = load_scale(ad, s + 3, G, M, N);
     }
-    dma_stage(ad, lds_a[buf], lds_b[buf], s + 2);    // s <= G-2: a valid stage
+    dma_stage(ad, lds_a[buf], lds_b[buf], s + 2);    // s <= G-2: a valid stage (past gb: unused)
     apply(T::kTM - 1, 1, acc[T::kTM - 1][1], sp[T::kTM - 1][1], s);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -345,12 +354,12 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
 #pragma unroll
     for (int j = 0; j < T::kTN; ++j) sb[j] = sbn[j];
   };
-  for (int s = 0; s < G - 1; ++s) int4_group(s);
+  for (int s = ga; s < gb; ++s) int4_group(s);
 
   // INT8 outlier group: stage G-1 (its packed operands are in pa / pb) and stage G (copied by
   // the last iteration), each two K=32 int8 MFMAs per tile; sa / sb hold the group's scales.
-  {
-    const int buf = G & 1;
+  if (last_split) {
+    const int buf = (G - ga) & 1;
     v16i acc[T::kTM][T::kTN];
     auto lo = [](v8i v) { return v4i{v[0], v[1], v[2], v[3]}; };
     auto hi = [](v8i v) { return v4i{v[4], v[5], v[6], v[7]}; };
@@ -375,6 +384,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
         for (int r = 0; r < 16; ++r) accf[r] = (float)acc[i][j][r];   // |acc| <= 128*127*127 < 2^24: exact
         finish_tile(i, j, accf, sa[i], sb[j], G - 1);
       }
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);                  // no copy into LDS outlives the workgroup
   }
 
   if (!kAcc) {
@@ -386,21 +397,68 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm * T::kWTM + i * 32 + (r >> 2) * 8 + kh * 4 + (r & 3);
           const int n = n0 + wn * T::kWTN + j * 32 + l32;
-          if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][r]));
+          if (m < M && n < N) {
+            if (splits == 1) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][r]));
+            else part[((size_t)split * M + m) * N + n] = yacc[i][j][r];
+          }
         }
+  }
+}
+
+// Y = fp16(0.5 * sum over splits of the partial sums), splits summed in order.  Four
+// elements per thread (M * N is not always a multiple of four: the tail is handled alone).
+__global__ __launch_bounds__(256) void gemm_splitk_finish_kernel(const float* __restrict__ part, int splits,
+                                                                 size_t count, uint16_t* __restrict__ Y) {
+  const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= count) return;
+  if (e + 4 <= count) {
+    float4 acc = *reinterpret_cast<const float4*>(part + e);
+    for (int k = 1; k < splits; ++k) {
+      const float4 v = *reinterpret_cast<const float4*>(part + (size_t)k * count + e);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    ushort4 o;
+    o.x = __half_as_ushort(__float2half_rn(0.5f * acc.x));
+    o.y = __half_as_ushort(__float2half_rn(0.5f * acc.y));
+    o.z = __half_as_ushort(__float2half_rn(0.5f * acc.z));
+    o.w = __half_as_ushort(__float2half_rn(0.5f * acc.w));
+    *reinterpret_cast<ushort4*>(Y + e) = o;
+  } else {
+    for (size_t t = e; t < count; ++t) {
+      float acc = part[t];
+      for (int k = 1; k < splits; ++k) acc += part[(size_t)k * count + t];
+      Y[t] = __half_as_ushort(__float2half_rn(0.5f * acc));
+    }
   }
 }
 
 // 128 x 128 workgroup tile, 2 x 2 waves of 64 x 64 (2 x 2 MFMA tiles of 32 x 32 each).
 constexpr int kBM = 128, kBN = 128, kWavesM = 2, kWavesN = 2;
+// Split-K: only when the tiles alone leave most of the 256 compute units idle; aims at about
+// one workgroup per compute unit, at least kSplitMinGroups INT4 groups per workgroup.
+constexpr int kSplitMinTiles = 128, kSplitTargetBlocks = 256, kSplitMinGroups = 4, kSplitMax = 8;
 
 }  // namespace
 
+int gemm_splits(int M, int N, int K) {
+  const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  const int G = K / ATOM_GROUP;
+  if (tiles >= kSplitMinTiles) return 1;
+  const int s = min(min((kSplitTargetBlocks + tiles - 1) / tiles, (G - 1) / kSplitMinGroups), kSplitMax);
+  return s < 2 ? 1 : s;
+}
+
 hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
-                       int K, uint16_t* Y, hipStream_t stream) {
-  const dim3 grid(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM));
-  hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, false>), grid, dim3(kWavesM * kWavesN * 64), 0,
-                     stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr);
+                       int K, uint16_t* Y, float* part, int splits, hipStream_t stream) {
+  const int tiles = ((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM);
+  hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, false>), dim3(tiles * splits),
+                     dim3(kWavesM * kWavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr, splits,
+                     part);
+  if (splits > 1) {
+    const size_t count = (size_t)M * N;
+    const size_t blocks = (count + 1023) / 1024;
+    hipLaunchKernelGGL(gemm_splitk_finish_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, splits, count, Y);
+  }
   return hipGetLastError();
 }
 
@@ -409,7 +467,7 @@ hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, in
   const dim3 grid(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM));
   hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, true>), grid, dim3(kWavesM * kWavesN * 64), 0,
                      stream, Xq, (const uint16_t*)nullptr, Wq, (const uint16_t*)nullptr, M, N, K,
-                     (uint16_t*)nullptr, acc);
+                     (uint16_t*)nullptr, acc, 1, (float*)nullptr);
   return hipGetLastError();
 }
 

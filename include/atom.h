@@ -124,6 +124,26 @@ int atom_gemm(const void *Xq, const void *sx, const void *Wq, const void *sw,
               int32_t M, int32_t N, int32_t K, void *Y, void *stream);
 
 /*
+ * Scratch for atom_gemm_ws: bytes of fp32 workspace that let atom_gemm_ws divide each tile's
+ * groups among several workgroups (split-K) when the M x N tiles alone would leave most of
+ * the GPU idle; 0 when no split is used for this shape; -ATOM_E_SHAPE for invalid shapes.
+ */
+int64_t atom_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
+/*
+ * atom_gemm with caller-provided scratch (the library allocates nothing).  With workspace
+ * != NULL and workspace_bytes >= atom_gemm_workspace_bytes(M, N, K) > 0, each split
+ * accumulates its groups in fp32 and a second kernel adds the splits in a fixed order and
+ * rounds once to fp16 (the sum over groups is then associated differently: results agree
+ * with atom_gemm to fp32 rounding, not bit for bit).  Otherwise it is exactly atom_gemm.
+ * The workspace must be 16-byte aligned and must not overlap any argument; its contents on
+ * entry do not matter and are overwritten.
+ */
+int atom_gemm_ws(const void *Xq, const void *sx, const void *Wq, const void *sw,
+                 int32_t M, int32_t N, int32_t K, void *Y, void *workspace,
+                 int64_t workspace_bytes, void *stream);
+
+/*
  * Per-group integer accumulators (verification aid): acc[g, m, n] = acc_g[m,n] as defined
  * for atom_gemm, computed by the same main loop.  acc is int32 [G, M, N] (output,
  * G*M*N*4 bytes).

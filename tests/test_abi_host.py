@@ -33,7 +33,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 9
+    assert len(names) == 11
     assert sorted(bq.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -148,3 +148,30 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setenv("ATOM_LIB", str(tmp_path / "nope.so"))
     with pytest.raises(bq.AtomError, match="not built"):
         bq.load_library()
+
+
+def test_gemm_workspace_query(lib):
+    # 256 x 4096 output = 2 x 32 tiles of 128 x 128: split four ways, fp32 partials
+    assert bq.atom_gemm_workspace_bytes(256, 4096, 4096) == 4 * 256 * 4096 * 4
+    assert bq.atom_gemm_workspace_bytes(64, 128, 4096) == 7 * 64 * 128 * 4     # capped by 31 INT4 groups / 4
+    assert bq.atom_gemm_workspace_bytes(1, 130, 1152) == 2 * 1 * 130 * 4
+    # enough tiles, or too few groups to divide: no scratch
+    assert bq.atom_gemm_workspace_bytes(2048, 4096, 11008) == 0
+    assert bq.atom_gemm_workspace_bytes(1024, 11008, 4096) == 0
+    assert bq.atom_gemm_workspace_bytes(4, 4, 256) == 0
+    assert lib.atom_gemm_workspace_bytes(4, 4, 200) == -E_SHAPE
+    assert lib.atom_gemm_workspace_bytes(0, 4, 256) == -E_SHAPE
+    with pytest.raises(bq.AtomError):
+        bq.atom_gemm_workspace_bytes(4, 4, 200)
+
+
+def test_gemm_ws_validation(lib):
+    g = lib.atom_gemm_ws
+    M, N, K = 64, 128, 4096
+    need = bq.atom_gemm_workspace_bytes(M, N, K)
+    F = 0x60000000
+    assert g(A, B, C, D, M, N, K, None, F, need, S) == E_NULL
+    assert g(A, B, C, D, M, N, 300, E, F, need, S) == E_SHAPE
+    assert g(A, B, C, D, M, N, K, E, F + 8, need, S) == E_ALIGN       # workspace used, misaligned
+    assert g(A, B, C, D, M, N, K, E, E + 64, need, S) == E_OVERLAP    # workspace over Y
+    assert g(A, B, C, D, M, N, K, E, A + 16, need, S) == E_OVERLAP    # workspace over Xq

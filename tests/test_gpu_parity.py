@@ -272,3 +272,40 @@ def test_deterministic_and_side_stream():
     s.synchronize()
     y2 = host(y2)
     np.testing.assert_array_equal(y1.view(np.uint16), y2.view(np.uint16))
+
+
+# --------------------------------------------------------------------------- split-K (atom_gemm_ws)
+SPLIT = [(64, 128, 4096), (200, 300, 2048), (1, 130, 1152), (256, 4096, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT)
+def test_gemm_ws_split_matches_oracle(M, N, K):
+    """Shapes with few tiles take the split-K path; Y stays within the oracle tolerance."""
+    need = bq.atom_gemm_workspace_bytes(M, N, K)
+    assert need > 0, "this shape is expected to split"
+    _say(f"[split-K] M={M} N={N} K={K} workspace={need}")
+    x, wt, _ = synth.make_linear(M, K, N, seed=3 * M + N + K)
+    perm = np.random.default_rng(K + 1).permutation(K).astype(np.int32)
+    Xd, Wd, Pd = dev(x), dev(wt), dev(perm)
+    Xq, sx = bq.atom_quantize_act(Xd, Pd)
+    Wq, sw = bq.atom_pack_weights(Wd, Pd)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")   # contents must not matter
+    Y = host(bq.atom_gemm_ws(Xq, sx, Wq, sw, K, ws))
+    qx, sxr = O.quantize_rows(x, perm)
+    qw, swr = O.quantize_rows(wt, perm)
+    assert_y_close(Y, O.gemm_ref(qx, sxr, qw, swr), f"split {M}x{N}x{K}")
+    Y2 = host(bq.atom_gemm_ws(Xq, sx, Wq, sw, K, ws))          # deterministic: splits summed in order
+    np.testing.assert_array_equal(Y.view(np.uint16), Y2.view(np.uint16))
+
+
+def test_gemm_ws_without_enough_scratch_is_atom_gemm():
+    M, N, K = 64, 128, 4096
+    x, wt, _ = synth.make_linear(M, K, N, seed=11)
+    perm = np.arange(K, dtype=np.int32)
+    Xq, sx = bq.atom_quantize_act(dev(x), dev(perm))
+    Wq, sw = bq.atom_pack_weights(dev(wt), dev(perm))
+    ref = host(bq.atom_gemm(Xq, sx, Wq, sw, K))
+    small = torch.empty(bq.atom_gemm_workspace_bytes(M, N, K) - 16, dtype=torch.uint8, device="cuda")
+    for ws in (None, small):
+        y = host(bq.atom_gemm_ws(Xq, sx, Wq, sw, K, ws))
+        np.testing.assert_array_equal(y.view(np.uint16), ref.view(np.uint16))
