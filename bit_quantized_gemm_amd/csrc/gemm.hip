@@ -78,17 +78,47 @@ __device__ __forceinline__ v8i fp8_odd(v8i w) {
   return r;
 }
 
+// The matrix-core calls below take the weight operand b as their first source and the
+// activation operand a as their second, so a 32x32 accumulator holds the output tile
+// transposed: lane l owns output row l & 31, and its element r is column
+// (r >> 2) * 8 + (l >> 5) * 4 + (r & 3), i.e. four runs of four consecutive columns that
+// the epilogue stores as vectors.
 __device__ __forceinline__ v16f mma_fp8(v8i a, v8i b, v16f c) {
   // cbsz = blgp = 0: both operands fp8 e4m3; opsel 0 and E8M0 scale 2^9 on both sides
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kScaleE8M0, 0, kScaleE8M0);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, kScaleE8M0, 0, kScaleE8M0);
 }
 
 __device__ __forceinline__ v16i mma_i8(v4i a, v4i b, v16i c) {
-  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c, 0, 0, 0);
 }
+
+// Output row (within a 32x32 tile) and first of four consecutive columns held by element
+// group q (elements 4q .. 4q+3) of a lane's accumulator.
+__device__ __forceinline__ int acc_row(int lane) { return lane & 31; }
+__device__ __forceinline__ int acc_col(int lane, int q) { return q * 8 + (lane >> 5) * 4; }
 
 // Chunk position swizzle of LDS row r (rows are 64 bytes)
 __device__ __forceinline__ int chunk_swz(int r) { return (r >> 2) & 3; }
+
+// s_waitcnt immediate (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8): wait until at
+// most n vector-memory operations of this wave are outstanding and all its LDS operations
+// have completed.  n = 63 leaves vector memory alone.
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// Workgroup barrier that does not wait for this wave's outstanding vector-memory operations
+// (__syncthreads would drain every copy in flight).  The empty asm statements keep the
+// compiler from moving memory operations across it; callers wait for what must be complete.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Compile-time ring position of a stage buffer.
+template <int P>
+struct Ring {
+  static constexpr int kCur = P, kNext = (P + 1) % 3;
+};
 
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
@@ -156,9 +186,14 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
     const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out,
     int splits, float* __restrict__ part) {
   using T = Tile<BM, BN, WAVES_M, WAVES_N>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_s[2][BM + BN];   // sx of the tile rows, then sw
+  // Three stage buffers, each its own object: the compiler then knows that a copy into one
+  // does not write what is read from another, and waits only where a buffer is really shared.
+  __shared__ __attribute__((aligned(16))) uint8_t la0[BM * kLdsRow], la1[BM * kLdsRow], la2[BM * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint8_t lb0[BN * kLdsRow], lb1[BN * kLdsRow], lb2[BN * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint16_t ls0[BM + BN], ls1[BM + BN], ls2[BM + BN];   // sx rows, then sw
+  auto LA = [&](int p) -> uint8_t* { return p == 0 ? la0 : p == 1 ? la1 : la2; };
+  auto LB = [&](int p) -> uint8_t* { return p == 0 ? lb0 : p == 1 ? lb1 : lb2; };
+  auto LS = [&](int p) -> uint16_t* { return p == 0 ? ls0 : p == 1 ? ls1 : ls2; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -215,11 +250,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   // term depends only on l32 (tile rows start at multiples of 32).
   const int lane_swz = chunk_swz(l32);
   const int a_row = (wm * T::kWTM + l32) * kLdsRow, b_row = (wn * T::kWTN + l32) * kLdsRow;
-  auto lds_a_chunk = [&](int buf, int i, int c) {
-    return *reinterpret_cast<const v4i*>(lds_a[buf] + a_row + i * 32 * kLdsRow + ((c ^ lane_swz) << 4));
-  };
-  auto lds_b_chunk = [&](int buf, int j, int c) {
-    return *reinterpret_cast<const v4i*>(lds_b[buf] + b_row + j * 32 * kLdsRow + ((c ^ lane_swz) << 4));
+  auto lds_chunk = [&](const uint8_t* buf, int row, int t, int c) {
+    return *reinterpret_cast<const v4i*>(buf + row + t * 32 * kLdsRow + ((c ^ lane_swz) << 4));
   };
   auto cat = [](v4i lo, v4i hi) { return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; };
 
@@ -227,30 +259,30 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   // (B) in K slot 0 of its half, so the f16 MFMA returns 2 * sx * sw exactly (two equal
   // exact products).  Every term of the Y accumulators thus carries the factor 2, which the
   // final store removes; a power of two changes no rounding.
-  auto read_scales = [&](int buf, h4 (&sa)[T::kTM], h4 (&sb)[T::kTN]) {
+  auto read_scales = [&](const uint16_t* ls, h4 (&sa)[T::kTM], h4 (&sb)[T::kTN]) {
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i) {
-      const uint16_t v = lds_s[buf][wm * T::kWTM + i * 32 + l32];
+      const uint16_t v = ls[wm * T::kWTM + i * 32 + l32];
       sa[i] = h4{__builtin_bit_cast(_Float16, v), (_Float16)0, (_Float16)0, (_Float16)0};
     }
 #pragma unroll
     for (int j = 0; j < T::kTN; ++j) {
-      const uint16_t v = lds_s[buf][BM + wn * T::kWTN + j * 32 + l32];
+      const uint16_t v = ls[BM + wn * T::kWTN + j * 32 + l32];
       sb[j] = h4{__builtin_bit_cast(_Float16, v), (_Float16)0, (_Float16)0, (_Float16)0};
     }
   };
 
   // Rank-one scale product 2 * sx (x) sw of tile (i, j), in the accumulator layout.
   auto scale_product = [&](h4 sai, h4 sbj) {
-    return kAcc ? v16f{} : __builtin_amdgcn_mfma_f32_32x32x8f16(sai, sbj, v16f{}, 0, 0, 0);
+    return kAcc ? v16f{} : __builtin_amdgcn_mfma_f32_32x32x8f16(sbj, sai, v16f{}, 0, 0, 0);
   };
   // Group sum of tile (i, j) -> Y accumulators (or, kAcc, to acc_out for group g).
   auto apply = [&](int i, int j, const v16f& acc, const v16f& sp, int g) {
     if (kAcc) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * T::kWTM + i * 32 + (r >> 2) * 8 + kh * 4 + (r & 3);
-        const int n = n0 + wn * T::kWTN + j * 32 + l32;
+        const int m = m0 + wm * T::kWTM + i * 32 + acc_row(lane);
+        const int n = n0 + wn * T::kWTN + j * 32 + acc_col(lane, r >> 2) + (r & 3);
         if (m < M && n < N) acc_out[((size_t)g * M + m) * N + n] = (int32_t)acc[r];   // exact integers
       }
     } else {
@@ -266,52 +298,81 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   // lane's row, chunks 2kh and 2kh+1 (stage bytes 32kh .. 32kh+31).  On an INT4 stage these
   // are 64 codes whose even and odd halves are the lane's K=32 slices of the two K=64 fp8
   // operands; on an INT8 stage, its K slices of two K=32 int8 operands.
-  auto read_packed = [&](int buf, v8i (&pa)[T::kTM], v8i (&pb)[T::kTN]) {
+  auto read_a = [&](const uint8_t* la, int i) {
+    return cat(lds_chunk(la, a_row, i, 2 * kh), lds_chunk(la, a_row, i, 2 * kh + 1));
+  };
+  auto read_b = [&](const uint8_t* lb, int j) {
+    return cat(lds_chunk(lb, b_row, j, 2 * kh), lds_chunk(lb, b_row, j, 2 * kh + 1));
+  };
+  auto read_packed = [&](const uint8_t* la, const uint8_t* lb, v8i (&pa)[T::kTM], v8i (&pb)[T::kTN]) {
 #pragma unroll
-    for (int i = 0; i < T::kTM; ++i) pa[i] = cat(lds_a_chunk(buf, i, 2 * kh), lds_a_chunk(buf, i, 2 * kh + 1));
+    for (int i = 0; i < T::kTM; ++i) pa[i] = read_a(la, i);
 #pragma unroll
-    for (int j = 0; j < T::kTN; ++j) pb[j] = cat(lds_b_chunk(buf, j, 2 * kh), lds_b_chunk(buf, j, 2 * kh + 1));
+    for (int j = 0; j < T::kTN; ++j) pb[j] = read_b(lb, j);
   };
 
-  // Stage s+1 (packed codes by LDS DMA, scales through a register loaded one stage earlier)
-  // is written during group s; `sreg` holds the scale of the next stage to write.
+  // Stage ring.  Stage t (t = ga, ga+1, ...) lives in LDS buffer (t - ga) % 3.  While group s
+  // is multiplied, its packed operands and scales are in registers; stage s+1 has landed and
+  // each wave reads it into the registers that group s's decode has just freed; the copies
+  // of stage s+2 (issued at the start of group s-1) and stage s+3 (issued at the start of
+  // group s, into the buffer stage s came from) are in flight.  The one barrier per group
+  // comes after this wave's copy of stage s+2 has landed and its reads of stage s+1 have
+  // completed: after it stage s+2 is visible to all and the buffer of stage s+1 may be
+  // refilled.  Scales take the same ring: each thread's scale of stage t is loaded into
+  // `sreg` during group t-4 and written to LDS at the start of group t-3.
+  constexpr int kPerStage = 2 * T::kDma + (kAcc ? 0 : 1);   // vector-memory operations per stage
   uint16_t sreg = 0;
-  if (!kAcc) sreg = load_scale(ad, ga, G, M, N);
-  dma_stage(ad, lds_a[0], lds_b[0], ga);
-  if (!kAcc) {
-    __builtin_amdgcn_s_waitcnt(0);
-    lds_s[0][tid] = sreg;
-    sreg = load_scale(ad, ga + 1, G, M, N);
+  {
+    uint16_t s0 = 0, s1 = 0, s2 = 0;
+    if (!kAcc) {
+      s0 = load_scale(ad, ga, G, M, N);
+      s1 = load_scale(ad, ga + 1, G, M, N);
+      s2 = load_scale(ad, ga + 2, G, M, N);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    dma_stage(ad, la0, lb0, ga);
+    dma_stage(ad, la1, lb1, min(ga + 1, G));
+    dma_stage(ad, la2, lb2, min(ga + 2, G));
+    __builtin_amdgcn_sched_barrier(0);
+    if (!kAcc) {
+      sreg = load_scale(ad, ga + 3, G, M, N);
+      ls0[tid] = s0;
+      ls1[tid] = s1;
+      ls2[tid] = s2;
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kPerStage));   // stages ga and ga+1 have landed
+    wg_barrier();
   }
-  __builtin_amdgcn_s_waitcnt(0);                    // this wave's copies have landed
-  __syncthreads();
-  // stage 1 into buffer 1 (nobody reads it before the first barrier of the loop)
-  if (!kAcc) {
-    lds_s[1][tid] = sreg;
-    sreg = load_scale(ad, ga + 2, G, M, N);
-  }
-  dma_stage(ad, lds_a[1], lds_b[1], ga + 1);         // ga + 1 <= G
   v8i pa[T::kTM], pb[T::kTN];
   h4 sa[T::kTM], sb[T::kTN];
-  if (!kAcc) read_scales(0, sa, sb);
-  read_packed(0, pa, pb);
+  if (!kAcc) read_scales(ls0, sa, sb);
+  read_packed(la0, lb0, pa, pb);
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));             // buffer 0 read by this wave
+  wg_barrier();                                                // ... and by all: it may be refilled
 
-  // INT4 groups s = 0 .. G-2, packed operands of group s already in registers.  A wave
-  // issues in order, so nothing may wait on the MFMA issued just before it.  Per tile row i:
-  // region a decodes A row i (and every B column at i = 0), applies tile (i-1, 0), issues
-  // the scale product of tile (i, 0) and the even-code MFMAs of tiles (i, 0) and (i, 1);
-  // region b applies tile (i-1, 1), issues the scale product of tile (i, 1) and the odd-code
-  // MFMAs of both tiles, each after an independent MFMA.  A tile's sums (two K=64 fp8 MFMAs:
-  // the exact group sum in fp32) and its scale product are complete when the next tile row
-  // applies them.  The scheduling fences keep this order.  The barrier at the end publishes
-  // stage s+1 (copied during the previous iteration); its operands are read right after it,
-  // then stage s+2 is copied into the buffer stage s came from, and the last tile row is
-  // applied meanwhile.
+  // INT4 group s in ring position P (stage s in buffer P).  A wave issues in order, so nothing
+  // may wait on the MFMA issued just before it.  Per tile row i: region a decodes A row i
+  // (and every B column at i = 0), reads the matching operands of stage s+1, applies tile
+  // (i-1, 0) (at i = 0: tile (kTM-1, 1) of group s-1, carried over), issues the scale product
+  // of tile (i, 0) and the even-code MFMAs of tiles (i, 0) and (i, 1); region b applies tile
+  // (i-1, 1), issues the scale product of tile (i, 1) and the odd-code MFMAs of both tiles,
+  // each after an independent MFMA.  A tile's sums (two K=64 fp8 MFMAs: the exact group sum
+  // in fp32) and its scale product are complete when they are applied.  The scheduling
+  // fences keep this order.
   static_assert(T::kTN == 2, "tile rows are processed as pairs of 32x32 tiles");
-  auto int4_group = [&](int s) {
-    const int buf = (s - ga) & 1;                    // stage s lives in buffer (s - ga) % 2
+  auto int4_group = [&](auto ring, int s) {
+    constexpr int p = decltype(ring)::kCur, pn = decltype(ring)::kNext;
+    // refill buffer p (stage s was read during group s-1, before the last barrier)
+    if (!kAcc) {
+      LS(p)[tid] = sreg;
+      sreg = load_scale(ad, s + 4, G, M, N);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    dma_stage(ad, LA(p), LB(p), min(s + 3, G));               // past the row end: unused
+    __builtin_amdgcn_sched_barrier(0);
     v16f acc[T::kTM][2], sp[T::kTM][2];
     v8i be[2], bo[2];
+    h4 san[T::kTM], sbn[T::kTN];
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i) {
       const v8i ae = fp8_even(pa[i]), ao = fp8_odd(pa[i]);
@@ -320,8 +381,11 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
         for (int j = 0; j < 2; ++j) {
           be[j] = fp8_even(pb[j]);
           bo[j] = fp8_odd(pb[j]);
+          pb[j] = read_b(LB(pn), j);
         }
+        if (!kAcc) read_scales(LS(pn), san, sbn);
       }
+      pa[i] = read_a(LA(pn), i);
       if (i > 0) apply(i - 1, 0, acc[i - 1][0], sp[i - 1][0], s);
       sp[i][0] = scale_product(sa[i], sb[0]);
       acc[i][0] = mma_fp8(ae, be[0], v16f{});
@@ -334,32 +398,28 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
       __builtin_amdgcn_sched_barrier(0);
     }
     apply(T::kTM - 1, 0, acc[T::kTM - 1][0], sp[T::kTM - 1][0], s);
-    h4 san[T::kTM], sbn[T::kTN];
-    __builtin_amdgcn_s_waitcnt(0);                  // this wave's copies of stage s+1 have landed
-    __syncthreads();
-    if (!kAcc) read_scales(buf ^ 1, san, sbn);       // first: LDS returns in order
-    read_packed(buf ^ 1, pa, pb);                    // group s+1 (INT8 half 0 when s = G-2)
-    // stage s+2 into buffer `buf`: its operands were read before this barrier; issued after
-    // the reads so that they need not wait for it, and the scale load first so that waiting
-    // for the copy covers it
-    if (!kAcc) {
-      lds_s[buf][tid] = sreg;
-      sreg = load_scale(ad, s + 3, G, M, N);
-    }
-    dma_stage(ad, lds_a[buf], lds_b[buf], s + 2);    // s <= G-2: a valid stage (past gb: unused)
     apply(T::kTM - 1, 1, acc[T::kTM - 1][1], sp[T::kTM - 1][1], s);
-    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kPerStage));   // own copy of stage s+2 landed, reads done
+    wg_barrier();
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i) sa[i] = san[i];
 #pragma unroll
     for (int j = 0; j < T::kTN; ++j) sb[j] = sbn[j];
   };
-  for (int s = ga; s < gb; ++s) int4_group(s);
+  {
+    int s = ga;
+    for (; s + 3 <= gb; s += 3) {
+      int4_group(Ring<0>{}, s);
+      int4_group(Ring<1>{}, s + 1);
+      int4_group(Ring<2>{}, s + 2);
+    }
+    if (s < gb) int4_group(Ring<0>{}, s++);
+    if (s < gb) int4_group(Ring<1>{}, s++);
+  }
 
-  // INT8 outlier group: stage G-1 (its packed operands are in pa / pb) and stage G (copied by
-  // the last iteration), each two K=32 int8 MFMAs per tile; sa / sb hold the group's scales.
+  // INT8 outlier group: stage G-1 (its packed operands are in pa / pb, the group's scales in
+  // sa / sb) and stage G (landed in buffer (G - ga) % 3), each two K=32 int8 MFMAs per tile.
   if (last_split) {
-    const int buf = (G - ga) & 1;
     v16i acc[T::kTM][T::kTN];
     auto lo = [](v8i v) { return v4i{v[0], v[1], v[2], v[3]}; };
     auto hi = [](v8i v) { return v4i{v[4], v[5], v[6], v[7]}; };
@@ -370,9 +430,10 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
         acc[i][j] = mma_i8(lo(pa[i]), lo(pb[j]), v16i{});
         acc[i][j] = mma_i8(hi(pa[i]), hi(pb[j]), acc[i][j]);
       }
-    __builtin_amdgcn_s_waitcnt(0);                  // stage G, copied by the last iteration
-    __syncthreads();
-    read_packed(buf, pa, pb);
+    const int pg = (G - ga) % 3;
+    if (pg == 0) read_packed(la0, lb0, pa, pb);
+    else if (pg == 1) read_packed(la1, lb1, pa, pb);
+    else read_packed(la2, lb2, pa, pb);
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i)
 #pragma unroll
@@ -384,24 +445,52 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
         for (int r = 0; r < 16; ++r) accf[r] = (float)acc[i][j][r];   // |acc| <= 128*127*127 < 2^24: exact
         finish_tile(i, j, accf, sa[i], sb[j], G - 1);
       }
-  } else {
-    __builtin_amdgcn_s_waitcnt(0);                  // no copy into LDS outlives the workgroup
   }
+  __builtin_amdgcn_s_waitcnt(0);                    // no copy into LDS outlives the workgroup
 
+  // Store.  Each lane writes four runs of four consecutive outputs per tile: 8-byte fp16
+  // stores (16-byte fp32 partials) when the tile lies inside Y and every row start is
+  // 8-byte aligned (N % 4 == 0), element by element otherwise.
   if (!kAcc) {
+    const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;   // uniform
+    if (vec) {
 #pragma unroll
-    for (int i = 0; i < T::kTM; ++i)
+      for (int i = 0; i < T::kTM; ++i) {
+        const size_t m = (size_t)(m0 + wm * T::kWTM + i * 32 + acc_row(lane));
 #pragma unroll
-      for (int j = 0; j < T::kTN; ++j)
+        for (int j = 0; j < T::kTN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * T::kWTM + i * 32 + (r >> 2) * 8 + kh * 4 + (r & 3);
-          const int n = n0 + wn * T::kWTN + j * 32 + l32;
-          if (m < M && n < N) {
-            if (splits == 1) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][r]));
-            else part[((size_t)split * M + m) * N + n] = yacc[i][j][r];
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn * T::kWTN + j * 32 + acc_col(lane, q);
+            const float v0 = yacc[i][j][4 * q], v1 = yacc[i][j][4 * q + 1];
+            const float v2 = yacc[i][j][4 * q + 2], v3 = yacc[i][j][4 * q + 3];
+            if (splits == 1) {
+              ushort4 o;
+              o.x = __half_as_ushort(__float2half_rn(0.5f * v0));
+              o.y = __half_as_ushort(__float2half_rn(0.5f * v1));
+              o.z = __half_as_ushort(__float2half_rn(0.5f * v2));
+              o.w = __half_as_ushort(__float2half_rn(0.5f * v3));
+              *reinterpret_cast<ushort4*>(Y + m * N + n) = o;
+            } else {
+              *reinterpret_cast<float4*>(part + ((size_t)split * M + m) * N + n) = float4{v0, v1, v2, v3};
+            }
           }
-        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < T::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::kTN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm * T::kWTM + i * 32 + acc_row(lane);
+            const int n = n0 + wn * T::kWTN + j * 32 + acc_col(lane, r >> 2) + (r & 3);
+            if (m < M && n < N) {
+              if (splits == 1) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][r]));
+              else part[((size_t)split * M + m) * N + n] = yacc[i][j][r];
+            }
+          }
+    }
   }
 }
 

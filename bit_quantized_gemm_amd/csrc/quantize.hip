@@ -9,7 +9,12 @@
 //
 // Work layout.  Persistent workgroups of 256 threads walk the rows.  A row is staged in LDS
 // (fp16, 16-byte loads); the next row's loads are issued into registers before the current
-// row is processed, so HBM reads overlap the arithmetic.  The gather offsets through perm are
+// row is processed, so HBM reads overlap the arithmetic.  The staged row is stored by
+// columns: original element e = 16q + r sits in 32-bit word (r / 2) * QP + q, half r % 2,
+// where QP >= K/16 is padded to 8 mod 64.  A thread reads 16 consecutive reordered elements,
+// which for neighbouring lanes lie 16 elements apart in the row, so the lanes of one read hit
+// consecutive words (distinct banks) instead of words 32 bytes apart, and the four 32-bit
+// writes of a 16-byte chunk from 64 lanes cover all 64 banks.  The gather offsets through perm are
 // computed once per workgroup and kept in registers (no memory traffic in the row loop, so
 // nothing else waits behind the prefetch).  Each thread gathers 16 consecutive
 // reordered elements through perm; a group of 128 is 8 neighbouring lanes, whose absmax is
@@ -46,6 +51,9 @@ constexpr int kLanesPerGroup = ATOM_GROUP / kPerThread;   // 8
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 
+// Column stride (32-bit words) of the staged row: the smallest value >= K/16 that is 8 mod 64.
+__host__ __device__ constexpr int staged_stride(int K) { return K / 16 + ((8 - K / 16) & 63); }
+
 // max over the 8 lanes of a group (lanes 8k..8k+7) via DPP: xor 1, xor 2 (quad perms), then
 // the half-row mirror (lane i <-> 7-i), which pairs the two quads of the group.
 __device__ __forceinline__ float group_max8(float a) {
@@ -81,8 +89,9 @@ template <int CHUNKS, int PASSES>
 __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* __restrict__ X,
                                                                 const int32_t* __restrict__ perm, int rows, int K,
                                                                 uint8_t* __restrict__ Q, uint16_t* __restrict__ S) {
-  extern __shared__ u32x4 lds_row4[];
-  const uint8_t* lds_bytes = reinterpret_cast<const uint8_t*>(lds_row4);
+  extern __shared__ uint32_t lds_words[];
+  const uint8_t* lds_bytes = reinterpret_cast<const uint8_t*>(lds_words);
+  const int QP = staged_stride(K);
   const int G = K / ATOM_GROUP;
   const int klo = K - ATOM_OUTLIERS;
   const size_t rb = (size_t)(klo / 2 + ATOM_OUTLIERS);
@@ -96,10 +105,10 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
 #pragma unroll
     for (int v = 0; v < kPerThread / 4; ++v) {
       const int4 p = *reinterpret_cast<const int4*>(perm + c + 4 * v);
-      off[4 * v] = 2 * (int)__builtin_elementwise_min((unsigned)p.x, kmax);
-      off[4 * v + 1] = 2 * (int)__builtin_elementwise_min((unsigned)p.y, kmax);
-      off[4 * v + 2] = 2 * (int)__builtin_elementwise_min((unsigned)p.z, kmax);
-      off[4 * v + 3] = 2 * (int)__builtin_elementwise_min((unsigned)p.w, kmax);
+      const unsigned e[4] = {__builtin_elementwise_min((unsigned)p.x, kmax), __builtin_elementwise_min((unsigned)p.y, kmax),
+                             __builtin_elementwise_min((unsigned)p.z, kmax), __builtin_elementwise_min((unsigned)p.w, kmax)};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) off[4 * v + u] = (int)((((e[u] & 15) >> 1) * QP + (e[u] >> 4)) * 4 + (e[u] & 1) * 2);
     }
   };
   int offs[PASSES > 0 ? PASSES : 1][kPerThread];
@@ -187,7 +196,14 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
       const int c = threadIdx.x + i * kThreads;
-      if (c < nchunks) lds_row4[c] = pre[i];
+      if (c < nchunks) {
+        // chunk c = elements 8c .. 8c+7 = words 4 (c % 2) .. 4 (c % 2) + 3 of column c / 2
+        uint32_t* w = lds_words + (c & 1) * 4 * QP + (c >> 1);
+        w[0] = pre[i].x;
+        w[QP] = pre[i].y;
+        w[2 * QP] = pre[i].z;
+        w[3 * QP] = pre[i].w;
+      }
     }
     __syncthreads();
     if (row + (int)gridDim.x < rows) prefetch(row + gridDim.x);   // next row's loads fly meanwhile
@@ -212,13 +228,13 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
 template <int CHUNKS, int PASSES>
 hipError_t launch_rq(const uint16_t* X, const int32_t* perm, int rows, int K, uint8_t* Q, uint16_t* S,
                      hipStream_t stream) {
-  const size_t lds = (size_t)K * sizeof(uint16_t);
+  const size_t lds = (size_t)staged_stride(K) * 8 * sizeof(uint32_t);
   static int per_cu = 0, cus = 0;                   // occupancy of this instantiation, filled on first use
   if (per_cu == 0) {
     int dev = 0, n = 0, b = 0;
     if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
       cus = n;
-    const size_t lds_max = (size_t)CHUNKS * 8 * kThreads * sizeof(uint16_t);   // largest row of this range
+    const size_t lds_max = (size_t)staged_stride(CHUNKS * 8 * kThreads) * 8 * sizeof(uint32_t);   // largest row of this range
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, row_quantize_kernel<CHUNKS, PASSES>, kThreads, lds_max) ==
             hipSuccess && b > 0)
       per_cu = b;
