@@ -61,6 +61,7 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 constexpr int kStageBytes = 64;          // bytes of one stage of a packed row
 constexpr int kLdsRow = 64;              // bytes of one staged (packed) row in LDS
 constexpr int kXcds = 8;                 // accelerator complex dies (each with its own L2)
+constexpr int kBandM = 8;                // tile rows per band of the tile order
 constexpr int kScaleE8M0 = 127 + 9;      // 2^9: the e4m3 subnormal q * 2^-9 counts as q
 
 __device__ __forceinline__ uint32_t rotr4(uint32_t w) { return __builtin_amdgcn_alignbit(w, w, 4); }
@@ -201,16 +202,21 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
   // Tile order: workgroups go to the 8 XCDs round-robin by id; renumber them so that each
-  // XCD gets a contiguous run of tiles, M fastest, so an XCD's L2 holds one slice of W.
-  const int tiles_m = (M + BM - 1) / BM;
-  const int ntiles = tiles_m * ((N + BN - 1) / BN);
+  // XCD gets a contiguous run of tiles.  Tiles are numbered in bands of kBandM tile rows, M
+  // fastest inside a band, so a run of 64 tiles is an 8 x 8 block: each XCD's L2 then sees
+  // 8 tile rows of X and 8 tile columns of W instead of every row of X.
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
   const int nblocks = ntiles * splits;
   const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
   const int q = nblocks / kXcds, rem = nblocks % kXcds;
   const int lin2 = xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
   const int lin = lin2 % ntiles, split = lin2 / ntiles;
-  const int m0 = (lin % tiles_m) * BM;
-  const int n0 = (lin / tiles_m) * BN;
+  const int band = lin / (kBandM * tiles_n), first_m = band * kBandM;
+  const int band_m = min(tiles_m - first_m, kBandM);     // tile rows in this band
+  const int in_band = lin - band * kBandM * tiles_n;
+  const int m0 = (first_m + in_band % band_m) * BM;
+  const int n0 = (in_band / band_m) * BN;
   const int G = K / ATOM_GROUP;
   // this workgroup's INT4 groups [ga, gb); the last split also takes the INT8 group
   const int ga = split * (G - 1) / splits, gb = (split + 1) * (G - 1) / splits;
