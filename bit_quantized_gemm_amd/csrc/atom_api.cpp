@@ -111,8 +111,7 @@ int atom_quantize_act(const void* X, const int32_t* perm, int32_t M, int32_t K, 
 
 int64_t atom_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
   if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return -(int64_t)ATOM_E_SHAPE;
-  const int splits = atom::gemm_splits(M, N, K);
-  return splits > 1 ? (int64_t)splits * M * N * 4 : 0;
+  return atom::gemm_workspace_bytes(atom::gemm_plan(M, N, K));
 }
 
 int atom_gemm_ws(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N, int32_t K,
@@ -120,19 +119,20 @@ int atom_gemm_ws(const void* Xq, const void* sx, const void* Wq, const void* sw,
   if (!Xq || !sx || !Wq || !sw || !Y) return ATOM_E_NULL;
   if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return ATOM_E_SHAPE;
   if (!aligned16(Xq) || !aligned16(sx) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y)) return ATOM_E_ALIGN;
-  int splits = atom::gemm_splits(M, N, K);
-  const int64_t need = splits > 1 ? (int64_t)splits * M * N * 4 : 0;
-  if (!workspace || workspace_bytes < need) splits = 1;   // too little scratch: one workgroup per tile
-  if (splits > 1 && !aligned16(workspace)) return ATOM_E_ALIGN;
+  atom::GemmPlan plan = atom::gemm_plan(M, N, K);
+  const int64_t need = atom::gemm_workspace_bytes(plan);
+  if (!workspace || workspace_bytes < need) plan = atom::GemmPlan{plan.full + plan.rem, 0, 1};   // one workgroup per tile
+  const bool split = plan.rem > 0;
+  if (split && !aligned16(workspace)) return ATOM_E_ALIGN;
   const uint64_t G = (uint64_t)K / ATOM_GROUP;
   const uint64_t rb = (uint64_t)atom_row_bytes(K);
   const Range in[4] = {range_of(Xq, (uint64_t)M * rb), range_of(sx, G * M * 2), range_of(Wq, (uint64_t)N * rb),
                        range_of(sw, G * N * 2)};
-  const Range out[2] = {range_of(Y, (uint64_t)M * N * 2), range_of(workspace, splits > 1 ? (uint64_t)need : 0)};
-  if (int s = check_overlap(in, 4, out, splits > 1 ? 2 : 1)) return s;
+  const Range out[2] = {range_of(Y, (uint64_t)M * N * 2), range_of(workspace, split ? (uint64_t)need : 0)};
+  if (int s = check_overlap(in, 4, out, split ? 2 : 1)) return s;
   return hip_status(atom::launch_gemm(static_cast<const uint8_t*>(Xq), static_cast<const uint16_t*>(sx),
                                       static_cast<const uint8_t*>(Wq), static_cast<const uint16_t*>(sw), M, N, K,
-                                      static_cast<uint16_t*>(Y), static_cast<float*>(workspace), splits,
+                                      static_cast<uint16_t*>(Y), static_cast<float*>(workspace), plan,
                                       static_cast<hipStream_t>(stream)));
 }
 

@@ -14,11 +14,19 @@ hipError_t launch_channel_stat(const uint16_t* X, int M, int K, double* stat, hi
 hipError_t launch_select_outliers(const double* stat, int K, int32_t* perm, hipStream_t stream);
 hipError_t launch_row_quantize(const uint16_t* X, const int32_t* perm, int rows, int K, uint8_t* Q,
                                uint16_t* S, hipStream_t stream);
-// Number of workgroups a tile's K range is divided among (1: no split-K).
-int gemm_splits(int M, int N, int K);
-// splits > 1: `part` holds splits * M * N floats of scratch; splits == 1: `part` unused.
+// Split-K plan of a GEMM: the first `full` output tiles (in the kernel's tile order) run whole;
+// each of the last `rem` tiles is divided into `splits` pieces along K, whose fp32 partial
+// tiles go to caller scratch and are added by a second kernel.  rem == 0: no split.  The
+// kernel takes any mix; gemm_plan returns either no split or every tile split.
+struct GemmPlan {
+  int full, rem, splits;
+};
+GemmPlan gemm_plan(int M, int N, int K);
+// Scratch bytes the plan needs (0 when nothing is split).
+int64_t gemm_workspace_bytes(const GemmPlan& plan);
+// `part` holds gemm_workspace_bytes(plan) bytes of scratch when plan.rem > 0, else unused.
 hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
-                       int K, uint16_t* Y, float* part, int splits, hipStream_t stream);
+                       int K, uint16_t* Y, float* part, const GemmPlan& plan, hipStream_t stream);
 hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K, int32_t* acc,
                                  hipStream_t stream);
 

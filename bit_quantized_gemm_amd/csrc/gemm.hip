@@ -136,6 +136,15 @@ struct Tile {
   static_assert(BM == BN && kDma * kWaves * 16 == BM, "each wave copies whole 16-row slabs of A and B");
 };
 
+// Tile order: tiles are numbered in bands of kBandM tile rows, M fastest inside a band, so a
+// run of 64 consecutive tiles is an 8 x 8 block.  Returns the tile's row and column index.
+__device__ __forceinline__ int2 tile_coords(int lin, int tiles_m, int tiles_n) {
+  const int band = lin / (kBandM * tiles_n), first_m = band * kBandM;
+  const int band_m = min(tiles_m - first_m, kBandM);     // tile rows in this band
+  const int in_band = lin - band * kBandM * tiles_n;
+  return int2{first_m + in_band % band_m, in_band / band_m};
+}
+
 // Per-thread addressing of the stage copy, fixed for the whole K loop.  Wave w copies tile
 // rows [w * BM / W, (w + 1) * BM / W) of A and the same rows of B (W waves), 16 rows per
 // LDS-DMA instruction: lane i of instruction h lands at LDS row r = w * BM / W + 16h + i / 4,
@@ -178,14 +187,15 @@ __device__ __forceinline__ uint16_t load_scale(const StageAddr<NDMA>& ad, int s,
 }
 
 // kAcc = false: Y output.  kAcc = true: write the per-group integer accumulators instead.
-// splits > 1 (Y output only): the INT4 groups of a tile are divided among `splits`
-// workgroups (the last one also takes the INT8 group), each writing its fp32 sum, still
-// carrying the factor 2 of the scale products, to part[split][m][n].
+// Split-K (Y output only): the first `full` tiles run whole; the INT4 groups of each of the
+// last `rem` tiles are divided among `splits` pieces (the last piece also takes the INT8
+// group), each writing its fp32 tile sum, still carrying the factor 2 of the scale
+// products, tile-major to part[(piece split * rem + tile - full) * BM * BN].
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool kAcc>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(kAcc ? 1 : 2))) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx, const uint8_t* __restrict__ Wq,
     const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out,
-    int splits, float* __restrict__ part) {
+    int full, int rem, int splits, float* __restrict__ part) {
   using T = Tile<BM, BN, WAVES_M, WAVES_N>;
   // Three stage buffers, each its own object: the compiler then knows that a copy into one
   // does not write what is read from another, and waits only where a buffer is really shared.
@@ -201,26 +211,34 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   const int wave = tid >> 6;
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
-  // Tile order: workgroups go to the 8 XCDs round-robin by id; renumber them so that each
-  // XCD gets a contiguous run of tiles.  Tiles are numbered in bands of kBandM tile rows, M
-  // fastest inside a band, so a run of 64 tiles is an 8 x 8 block: each XCD's L2 then sees
-  // 8 tile rows of X and 8 tile columns of W instead of every row of X.
+  // Work assignment.  Workgroups go to the 8 XCDs round-robin by id.  Each XCD gets an equal
+  // share of the split pieces followed by an equal share of the whole tiles, each share a
+  // contiguous run in tile order (so an XCD's L2 sees a compact block of X and W), and the
+  // pieces are dispatched first so that the whole tiles fill in behind them.
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int ntiles = tiles_m * tiles_n;
-  const int nblocks = ntiles * splits;
+  const int npieces = rem * splits;
+  const int nblocks = full + npieces;
   const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
-  const int q = nblocks / kXcds, rem = nblocks % kXcds;
-  const int lin2 = xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
-  const int lin = lin2 % ntiles, split = lin2 / ntiles;
-  const int band = lin / (kBandM * tiles_n), first_m = band * kBandM;
-  const int band_m = min(tiles_m - first_m, kBandM);     // tile rows in this band
-  const int in_band = lin - band * kBandM * tiles_n;
-  const int m0 = (first_m + in_band % band_m) * BM;
-  const int n0 = (in_band / band_m) * BN;
+  const int qb = nblocks / kXcds, rb = nblocks % kXcds;   // workgroups on XCD x: qb + (x < rb)
+  const int qp = npieces / kXcds, rp = npieces % kXcds;   // pieces on XCD x: qp + (x < rp)
+  const int px = qp + (xcd < rp ? 1 : 0);
+  const int pbase = xcd * qp + min(xcd, rp);
+  int lin, split = 0, nsplit = 1;
+  if (local < px) {
+    const int piece = pbase + local;
+    lin = full + piece % rem;
+    split = piece / rem;
+    nsplit = splits;
+  } else {
+    lin = (xcd * qb + min(xcd, rb)) - pbase + (local - px);
+  }
+  const bool is_piece = nsplit > 1;
+  const int2 tc = tile_coords(lin, tiles_m, tiles_n);
+  const int m0 = tc.x * BM, n0 = tc.y * BN;
   const int G = K / ATOM_GROUP;
-  // this workgroup's INT4 groups [ga, gb); the last split also takes the INT8 group
-  const int ga = split * (G - 1) / splits, gb = (split + 1) * (G - 1) / splits;
-  const bool last_split = split == splits - 1;
+  // this workgroup's INT4 groups [ga, gb); the last piece also takes the INT8 group
+  const int ga = split * (G - 1) / nsplit, gb = (split + 1) * (G - 1) / nsplit;
+  const bool last_split = split == nsplit - 1;
   const int S = G + 1;                                  // stages per row
   const size_t rbytes = (size_t)S * kStageBytes;        // = (K-128)/2 + 128
   const int l32 = lane & 31;                            // row (A) / column (B) inside a 32x32 tile
@@ -454,12 +472,27 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   }
   __builtin_amdgcn_s_waitcnt(0);                    // no copy into LDS outlives the workgroup
 
-  // Store.  Each lane writes four runs of four consecutive outputs per tile: 8-byte fp16
-  // stores (16-byte fp32 partials) when the tile lies inside Y and every row start is
-  // 8-byte aligned (N % 4 == 0), element by element otherwise.
+  // Store.  Each lane writes four runs of four consecutive outputs per tile.  A split piece
+  // writes its whole fp32 tile (16-byte stores; rows and columns past Y land in the piece's
+  // own scratch tile and are never read).  A whole tile writes Y with 8-byte fp16 stores when
+  // it lies inside Y and every row start is 8-byte aligned (N % 4 == 0), element by element
+  // otherwise.
   if (!kAcc) {
-    const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;   // uniform
-    if (vec) {
+    if (is_piece) {
+      float* tile = part + ((size_t)split * rem + (lin - full)) * (BM * BN);
+#pragma unroll
+      for (int i = 0; i < T::kTM; ++i) {
+        const int r = wm * T::kWTM + i * 32 + acc_row(lane);
+#pragma unroll
+        for (int j = 0; j < T::kTN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = wn * T::kWTN + j * 32 + acc_col(lane, q);
+            *reinterpret_cast<float4*>(tile + r * BN + c) =
+                float4{yacc[i][j][4 * q], yacc[i][j][4 * q + 1], yacc[i][j][4 * q + 2], yacc[i][j][4 * q + 3]};
+          }
+      }
+    } else if (m0 + BM <= M && n0 + BN <= N && (N & 3) == 0) {   // uniform
 #pragma unroll
       for (int i = 0; i < T::kTM; ++i) {
         const size_t m = (size_t)(m0 + wm * T::kWTM + i * 32 + acc_row(lane));
@@ -468,18 +501,12 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int n = n0 + wn * T::kWTN + j * 32 + acc_col(lane, q);
-            const float v0 = yacc[i][j][4 * q], v1 = yacc[i][j][4 * q + 1];
-            const float v2 = yacc[i][j][4 * q + 2], v3 = yacc[i][j][4 * q + 3];
-            if (splits == 1) {
-              ushort4 o;
-              o.x = __half_as_ushort(__float2half_rn(0.5f * v0));
-              o.y = __half_as_ushort(__float2half_rn(0.5f * v1));
-              o.z = __half_as_ushort(__float2half_rn(0.5f * v2));
-              o.w = __half_as_ushort(__float2half_rn(0.5f * v3));
-              *reinterpret_cast<ushort4*>(Y + m * N + n) = o;
-            } else {
-              *reinterpret_cast<float4*>(part + ((size_t)split * M + m) * N + n) = float4{v0, v1, v2, v3};
-            }
+            ushort4 o;
+            o.x = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][4 * q]));
+            o.y = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][4 * q + 1]));
+            o.z = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][4 * q + 2]));
+            o.w = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][4 * q + 3]));
+            *reinterpret_cast<ushort4*>(Y + m * N + n) = o;
           }
       }
     } else {
@@ -491,69 +518,77 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
           for (int r = 0; r < 16; ++r) {
             const int m = m0 + wm * T::kWTM + i * 32 + acc_row(lane);
             const int n = n0 + wn * T::kWTN + j * 32 + acc_col(lane, r >> 2) + (r & 3);
-            if (m < M && n < N) {
-              if (splits == 1) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][r]));
-              else part[((size_t)split * M + m) * N + n] = yacc[i][j][r];
-            }
+            if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][r]));
           }
-    }
-  }
-}
-
-// Y = fp16(0.5 * sum over splits of the partial sums), splits summed in order.  Four
-// elements per thread (M * N is not always a multiple of four: the tail is handled alone).
-__global__ __launch_bounds__(256) void gemm_splitk_finish_kernel(const float* __restrict__ part, int splits,
-                                                                 size_t count, uint16_t* __restrict__ Y) {
-  const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (e >= count) return;
-  if (e + 4 <= count) {
-    float4 acc = *reinterpret_cast<const float4*>(part + e);
-    for (int k = 1; k < splits; ++k) {
-      const float4 v = *reinterpret_cast<const float4*>(part + (size_t)k * count + e);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    ushort4 o;
-    o.x = __half_as_ushort(__float2half_rn(0.5f * acc.x));
-    o.y = __half_as_ushort(__float2half_rn(0.5f * acc.y));
-    o.z = __half_as_ushort(__float2half_rn(0.5f * acc.z));
-    o.w = __half_as_ushort(__float2half_rn(0.5f * acc.w));
-    *reinterpret_cast<ushort4*>(Y + e) = o;
-  } else {
-    for (size_t t = e; t < count; ++t) {
-      float acc = part[t];
-      for (int k = 1; k < splits; ++k) acc += part[(size_t)k * count + t];
-      Y[t] = __half_as_ushort(__float2half_rn(0.5f * acc));
     }
   }
 }
 
 // 128 x 128 workgroup tile, 2 x 2 waves of 64 x 64 (2 x 2 MFMA tiles of 32 x 32 each).
 constexpr int kBM = 128, kBN = 128, kWavesM = 2, kWavesN = 2;
-// Split-K: only when the tiles alone leave most of the 256 compute units idle; aims at about
-// one workgroup per compute unit, at least kSplitMinGroups INT4 groups per workgroup.
+// Split-K.  Grids of fewer than kSplitMinTiles tiles split every tile, aiming at about one
+// workgroup per compute unit; a piece keeps at least kSplitMinGroups INT4 groups.  Larger
+// grids are not split, not even a last partial round of tiles: with every compute unit busy
+// the chip runs at its power limit, so spreading a tail lowers the clock about as much as it
+// adds parallelism, and the partial sums and the second kernel are pure cost (measured:
+// 1024 x 4096 x 11008 with its last 176 of 688 tiles split in two spans the same time, and
+// 600 x 2048 x 15300 with 88 of 600 split three ways is slower).
 constexpr int kSplitMinTiles = 128, kSplitTargetBlocks = 256, kSplitMinGroups = 4, kSplitMax = 8;
+
+// Y of the split tiles = fp16(0.5 * sum over pieces of the partial tiles), pieces added in
+// order.  blockIdx.y = split tile (tile full + blockIdx.y in tile order); four consecutive
+// outputs of one tile row per thread.
+__global__ __launch_bounds__(256) void gemm_splitk_finish_kernel(const float* __restrict__ part, int full, int rem,
+                                                                 int splits, int M, int N, uint16_t* __restrict__ Y) {
+  const int t = blockIdx.y;
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;       // element of the tile, < kBM * kBN
+  const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+  const int2 tc = tile_coords(full + t, tiles_m, tiles_n);
+  const int m = tc.x * kBM + e / kBN, n = tc.y * kBN + e % kBN;
+  const float* src = part + (size_t)t * (kBM * kBN) + e;
+  float4 acc = *reinterpret_cast<const float4*>(src);
+  for (int k = 1; k < splits; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(src + (size_t)k * rem * (kBM * kBN));
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  if (m >= M) return;
+  const uint16_t o[4] = {__half_as_ushort(__float2half_rn(0.5f * acc.x)), __half_as_ushort(__float2half_rn(0.5f * acc.y)),
+                         __half_as_ushort(__float2half_rn(0.5f * acc.z)), __half_as_ushort(__float2half_rn(0.5f * acc.w))};
+  uint16_t* dst = Y + (size_t)m * N + n;
+  if (n + 4 <= N && (N & 3) == 0) {
+    *reinterpret_cast<ushort4*>(dst) = ushort4{o[0], o[1], o[2], o[3]};
+  } else {
+    for (int i = 0; i < 4; ++i)
+      if (n + i < N) dst[i] = o[i];
+  }
+}
 
 }  // namespace
 
-int gemm_splits(int M, int N, int K) {
+GemmPlan gemm_plan(int M, int N, int K) {
   const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   const int G = K / ATOM_GROUP;
-  if (tiles >= kSplitMinTiles) return 1;
+  if (tiles >= kSplitMinTiles) return GemmPlan{tiles, 0, 1};
   const int s = min(min((kSplitTargetBlocks + tiles - 1) / tiles, (G - 1) / kSplitMinGroups), kSplitMax);
-  return s < 2 ? 1 : s;
+  return s < 2 ? GemmPlan{tiles, 0, 1} : GemmPlan{0, tiles, s};
+}
+
+int64_t gemm_workspace_bytes(const GemmPlan& plan) {
+  return plan.rem > 0 ? (int64_t)plan.rem * plan.splits * kBM * kBN * (int64_t)sizeof(float) : 0;
 }
 
 hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
-                       int K, uint16_t* Y, float* part, int splits, hipStream_t stream) {
-  const int tiles = ((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM);
-  hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, false>), dim3(tiles * splits),
-                     dim3(kWavesM * kWavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr, splits,
-                     part);
-  if (splits > 1) {
-    const size_t count = (size_t)M * N;
-    const size_t blocks = (count + 1023) / 1024;
-    hipLaunchKernelGGL(gemm_splitk_finish_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, splits, count, Y);
-  }
+                       int K, uint16_t* Y, float* part, const GemmPlan& plan, hipStream_t stream) {
+  const int blocks = plan.full + plan.rem * plan.splits;
+  hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, false>), dim3(blocks),
+                     dim3(kWavesM * kWavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr,
+                     plan.full, plan.rem, plan.splits, part);
+  if (plan.rem > 0)
+    hipLaunchKernelGGL(gemm_splitk_finish_kernel, dim3(kBM * kBN / 4 / 256, plan.rem), dim3(256), 0, stream, part,
+                       plan.full, plan.rem, plan.splits, M, N, Y);
   return hipGetLastError();
 }
 
@@ -562,7 +597,7 @@ hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, in
   const dim3 grid(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM));
   hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, true>), grid, dim3(kWavesM * kWavesN * 64), 0,
                      stream, Xq, (const uint16_t*)nullptr, Wq, (const uint16_t*)nullptr, M, N, K,
-                     (uint16_t*)nullptr, acc, 1, (float*)nullptr);
+                     (uint16_t*)nullptr, acc, (int)grid.x, 0, 1, (float*)nullptr);
   return hipGetLastError();
 }
 

@@ -151,14 +151,19 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 
 def test_gemm_workspace_query(lib):
-    # 256 x 4096 output = 2 x 32 tiles of 128 x 128: split four ways, fp32 partials
-    assert bq.atom_gemm_workspace_bytes(256, 4096, 4096) == 4 * 256 * 4096 * 4
-    assert bq.atom_gemm_workspace_bytes(64, 128, 4096) == 7 * 64 * 128 * 4     # capped by 31 INT4 groups / 4
-    assert bq.atom_gemm_workspace_bytes(1, 130, 1152) == 2 * 1 * 130 * 4
-    # enough tiles, or too few groups to divide: no scratch
+    # fp32 partial tiles of 128 x 128, tile-major: bytes = split tiles x pieces x 64 KiB
+    T = 128 * 128 * 4
+    # 256 x 4096 output = 2 x 32 tiles: every tile split four ways
+    assert bq.atom_gemm_workspace_bytes(256, 4096, 4096) == 64 * 4 * T
+    assert bq.atom_gemm_workspace_bytes(64, 128, 4096) == 1 * 7 * T       # capped by 31 INT4 groups / 4
+    assert bq.atom_gemm_workspace_bytes(1, 130, 1152) == 2 * 2 * T
+    assert bq.atom_gemm_workspace_bytes(127 * 128, 128, 256 * 128) == 127 * 3 * T   # ceil(256 / 127) = 3
+    # 128 tiles or more, or too few groups to divide: no scratch
+    assert bq.atom_gemm_workspace_bytes(128 * 128, 128, 4096) == 0
     assert bq.atom_gemm_workspace_bytes(2048, 4096, 11008) == 0
     assert bq.atom_gemm_workspace_bytes(1024, 11008, 4096) == 0
     assert bq.atom_gemm_workspace_bytes(4, 4, 256) == 0
+    assert bq.atom_gemm_workspace_bytes(4, 4, 1024) == 0                    # 7 INT4 groups: one piece of 4
     assert lib.atom_gemm_workspace_bytes(4, 4, 200) == -E_SHAPE
     assert lib.atom_gemm_workspace_bytes(0, 4, 256) == -E_SHAPE
     with pytest.raises(bq.AtomError):

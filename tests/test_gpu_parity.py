@@ -309,3 +309,4 @@ def test_gemm_ws_without_enough_scratch_is_atom_gemm():
     for ws in (None, small):
         y = host(bq.atom_gemm_ws(Xq, sx, Wq, sw, K, ws))
         np.testing.assert_array_equal(y.view(np.uint16), ref.view(np.uint16))
+
