@@ -55,12 +55,15 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) { return __half2
 __host__ __device__ constexpr int staged_stride(int K) { return K / 16 + ((8 - K / 16) & 63); }
 
 // max over the 8 lanes of a group (lanes 8k..8k+7) via DPP: xor 1, xor 2 (quad perms), then
-// the half-row mirror (lane i <-> 7-i), which pairs the two quads of the group.
+// the half-row mirror (lane i <-> 7-i), which pairs the two quads of the group.  The values
+// are absolute values (sign bit clear), whose order as unsigned integers is their order as
+// floats, so the maximum is taken on the bits.
 __device__ __forceinline__ float group_max8(float a) {
-  a = __builtin_fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false)));
-  a = __builtin_fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0x4E, 0xF, 0xF, false)));
-  a = __builtin_fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0x141, 0xF, 0xF, false)));
-  return a;
+  unsigned u = __builtin_bit_cast(unsigned, a);
+  u = max(u, (unsigned)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false));
+  u = max(u, (unsigned)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, false));
+  u = max(u, (unsigned)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, u);
 }
 
 // Clamped quotient of x for scale s (> 0) with reciprocal r; its nearest integer (ties to
@@ -146,15 +149,12 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
     const float qmax = tail ? 127.0f : 7.0f;
     const __half s16 = __float2half_rn(a / qmax);      // correctly rounded fp32 divide, then RNE to fp16
     const float s = __half2float(s16);
+    // s == 0 (an all-zero group, or a scale that underflows fp16): r = 0 makes every code 0,
+    // since then t = 0, e = x, u = 0 for the group's (zero) elements; no branch needed
+    const float r = s > 0.0f ? 1.0f / s : 0.0f;
     float v[kPerThread];
-    if (s > 0.0f) {
-      const float r = 1.0f / s;
 #pragma unroll
-      for (int i = 0; i < kPerThread; ++i) v[i] = code_value(x[i], s, r, qmax);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kPerThread; ++i) v[i] = 0.0f;
-    }
+    for (int i = 0; i < kPerThread; ++i) v[i] = code_value(x[i], s, r, qmax);
     uint32_t b[kPerThread];                              // two's-complement code in the low byte
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) b[i] = __float_as_uint(v[i] + kRound);
