@@ -172,7 +172,7 @@ def main():
     ap.add_argument("--workload", default="llama7b", choices=sorted(WORKLOAD_SETS))
     ap.add_argument("--rotate", type=int, default=4, help="resident input copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="rows per shape in the CPU oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="rows per shape in the CPU oracle sample (2048: every row)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (steps times), to calibrate HBM byte counters")
     args = ap.parse_args()
