@@ -111,7 +111,7 @@ int atom_quantize_act(const void* X, const int32_t* perm, int32_t M, int32_t K, 
 
 int64_t atom_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
   if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return -(int64_t)ATOM_E_SHAPE;
-  return atom::gemm_workspace_bytes(atom::gemm_plan(M, N, K));
+  return atom::gemm_workspace_bytes(atom::gemm_plan(M, N, K), M, N);
 }
 
 int atom_gemm_ws(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N, int32_t K,
@@ -120,9 +120,12 @@ int atom_gemm_ws(const void* Xq, const void* sx, const void* Wq, const void* sw,
   if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return ATOM_E_SHAPE;
   if (!aligned16(Xq) || !aligned16(sx) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y)) return ATOM_E_ALIGN;
   atom::GemmPlan plan = atom::gemm_plan(M, N, K);
-  const int64_t need = atom::gemm_workspace_bytes(plan);
-  if (!workspace || workspace_bytes < need) plan = atom::GemmPlan{plan.full + plan.rem, 0, 1};   // one workgroup per tile
-  const bool split = plan.rem > 0;
+  int64_t need = atom::gemm_workspace_bytes(plan, M, N);
+  if (need > 0 && (!workspace || workspace_bytes < need)) {   // too little scratch: the 128 x 128 kernel, unsplit
+    plan = atom::GemmPlan{((M + 127) / 128) * ((N + 127) / 128), 0, 1, 0};
+    need = 0;
+  }
+  const bool split = need > 0;
   if (split && !aligned16(workspace)) return ATOM_E_ALIGN;
   const uint64_t G = (uint64_t)K / ATOM_GROUP;
   const uint64_t rb = (uint64_t)atom_row_bytes(K);

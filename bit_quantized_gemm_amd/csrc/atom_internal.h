@@ -18,15 +18,22 @@ hipError_t launch_row_quantize(const uint16_t* X, const int32_t* perm, int rows,
 // each of the last `rem` tiles is divided into `splits` pieces along K, whose fp32 partial
 // tiles go to caller scratch and are added by a second kernel.  rem == 0: no split.  The
 // kernel takes any mix; gemm_plan returns either no split or every tile split.
+// small != 0 instead selects the few-rows kernel (gemm_small.hip), which needs no scratch.
 struct GemmPlan {
   int full, rem, splits;
+  int small;
 };
+// Few-rows kernel: at most kSmallMaxM token rows, at most kSmallMaxGroups INT4 groups per K range.
+constexpr int kSmallMaxM = 16, kSmallMaxGroups = 4;
 GemmPlan gemm_plan(int M, int N, int K);
-// Scratch bytes the plan needs (0 when nothing is split).
-int64_t gemm_workspace_bytes(const GemmPlan& plan);
-// `part` holds gemm_workspace_bytes(plan) bytes of scratch when plan.rem > 0, else unused.
+// Scratch bytes the plan needs (0 when it writes Y directly).
+int64_t gemm_workspace_bytes(const GemmPlan& plan, int M, int N);
+// `part` holds gemm_workspace_bytes(plan, M, N) bytes of scratch when that is > 0, else unused.
 hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
                        int K, uint16_t* Y, float* part, const GemmPlan& plan, hipStream_t stream);
+// Few-rows kernel (M <= kSmallMaxM), Y written directly.
+hipError_t launch_gemm_small(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M,
+                             int N, int K, uint16_t* Y, hipStream_t stream);
 hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K, int32_t* acc,
                                  hipStream_t stream);
 

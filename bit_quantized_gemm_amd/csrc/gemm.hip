@@ -571,17 +571,20 @@ __global__ __launch_bounds__(256) void gemm_splitk_finish_kernel(const float* __
 GemmPlan gemm_plan(int M, int N, int K) {
   const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   const int G = K / ATOM_GROUP;
-  if (tiles >= kSplitMinTiles) return GemmPlan{tiles, 0, 1};
+  if (M <= kSmallMaxM) return GemmPlan{0, 0, 1, 1};
+  if (tiles >= kSplitMinTiles) return GemmPlan{tiles, 0, 1, 0};
   const int s = min(min((kSplitTargetBlocks + tiles - 1) / tiles, (G - 1) / kSplitMinGroups), kSplitMax);
-  return s < 2 ? GemmPlan{tiles, 0, 1} : GemmPlan{0, tiles, s};
+  return s < 2 ? GemmPlan{tiles, 0, 1, 0} : GemmPlan{0, tiles, s, 0};
 }
 
-int64_t gemm_workspace_bytes(const GemmPlan& plan) {
+int64_t gemm_workspace_bytes(const GemmPlan& plan, int M, int N) {
+  if (plan.small) return 0;
   return plan.rem > 0 ? (int64_t)plan.rem * plan.splits * kBM * kBN * (int64_t)sizeof(float) : 0;
 }
 
 hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
                        int K, uint16_t* Y, float* part, const GemmPlan& plan, hipStream_t stream) {
+  if (plan.small) return launch_gemm_small(Xq, sx, Wq, sw, M, N, K, Y, stream);
   const int blocks = plan.full + plan.rem * plan.splits;
   hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, false>), dim3(blocks),
                      dim3(kWavesM * kWavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr,

@@ -1,0 +1,166 @@
+// W4A4 GEMM for few token rows (M <= 16, the decode regime) on gfx950.
+//
+// Same product as gemm.hip (per 128-channel group g: an exact integer dot product of the
+// codes, scaled by sx[g,m] * sw[g,n] in fp32 and summed over groups; quantization record of
+// "Atom: Low-bit Quantization for Efficient and Accurate LLM Serving", Fields "Bits",
+// "Weight group size", "notes"), organised for a different bound.  With at most 16 rows of
+// activations every weight byte is used at most 16 times, so the time to beat is that of
+// reading the packed weights once from HBM; 128 x 128 tiles would waste 7/8 of every MFMA and
+// leave the copies latency-bound.
+//
+// Work layout.  A workgroup owns 16 output columns.  K is cut into ranges of at most
+// kSmallMaxGroups INT4 groups (the last range also takes the INT8 outlier group); the
+// workgroup has one wave per range, at most 16, and a wave takes every 16th range when there
+// are more.  A wave issues every load of a range at once straight into registers (no LDS
+// staging, no barrier), then runs one 16 x 16 x 128 fp8 MFMA per group.  At the end the waves'
+// fp32 sums meet in LDS and wave 0 adds them in wave order and writes Y: one kernel, no
+// scratch, deterministic.
+//
+// Operands.  Lane l supplies row (A: weight column n0 + l % 16; B: token row l % 16) and the
+// 32-byte K slice l / 16 of each operand.  Slices 0 and 1 take the even codes of packed bytes
+// 0-31 and 32-63 of the group's 64-byte stage (w & 0x87878787: fp8 e4m3 subnormals q * 2^-9),
+// slices 2 and 3 the odd codes of the same bytes (rotr(w, 4) & 0x87878787); both operands use
+// the same assignment, so every code of the group meets its partner once.  With the weights
+// as the first operand the 16 x 16 accumulator holds the output transposed: lane l owns token
+// row l % 16 and the four consecutive output columns 4 (l / 16) .. 4 (l / 16) + 3.
+//
+// Scales.  v_mfma_f32_16x16x16_f16 with each lane's fp16 scale in element 0 of its four
+// K values gives 4 * sw * sx exactly (four equal exact products) in the accumulator layout;
+// the factor 4 is removed at the end (a power of two: no rounding).
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "atom_internal.h"
+
+namespace atom {
+namespace {
+
+typedef int32_t v8i __attribute__((ext_vector_type(8)));
+typedef int32_t v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCols = 16;                    // output columns per workgroup
+constexpr uint32_t kFp8Mask = 0x87878787u;   // sign bit and 3-bit magnitude of each byte
+constexpr int kScaleE8M0 = 127 + 9;          // 2^9: the e4m3 subnormal q * 2^-9 counts as q
+
+// 32 packed bytes (two 16-byte loads) -> 32 fp8 operand bytes: the even codes (rot = 0) or the
+// odd codes (rot = 4) of each 32-bit word.
+__device__ __forceinline__ v8i decode32(uint4 lo, uint4 hi, int rot) {
+  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  v8i r;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r[k] = (int)(__builtin_amdgcn_alignbit(w[k], w[k], rot) & kFp8Mask);
+  return r;
+}
+
+__device__ __forceinline__ h4 scale_operand(uint16_t v) {
+  return h4{__builtin_bit_cast(_Float16, v), (_Float16)0, (_Float16)0, (_Float16)0};
+}
+
+constexpr int kMaxWaves = 16;                // waves (K ranges in flight) per workgroup
+
+// blockIdx.x: column block (columns n0 = 16 blockIdx.x ..); wave w handles K ranges w, w + waves, ...
+__global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const uint8_t* __restrict__ Xq,
+                                                                         const uint16_t* __restrict__ sx,
+                                                                         const uint8_t* __restrict__ Wq,
+                                                                         const uint16_t* __restrict__ sw, int M,
+                                                                         int N, int K, int ranges,
+                                                                         uint16_t* __restrict__ Y) {
+  __shared__ v4f red[kMaxWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+  const int r = lane & 15, slice = lane >> 4;
+  const int G = K / ATOM_GROUP;
+  const size_t rb = (size_t)(K - ATOM_OUTLIERS) / 2 + ATOM_OUTLIERS;
+  const int n0 = blockIdx.x * kCols;
+  // rows past N / M repeat the last valid one; their results are never stored
+  const int n = min(n0 + r, N - 1), m = min(r, M - 1);
+  const uint8_t* wrow = Wq + (size_t)n * rb + 32 * (slice & 1);
+  const uint8_t* xrow = Xq + (size_t)m * rb + 32 * (slice & 1);
+  const int rot = 4 * (slice >> 1);
+
+  v4f yacc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int range = wave; range < ranges; range += waves) {
+    const int ga = range * (G - 1) / ranges, gb = (range + 1) * (G - 1) / ranges;   // 1 .. kSmallMaxGroups
+    const int ng = gb - ga;                                                         // uniform
+    // every load of the range, issued before any of it is used
+    uint4 wl[kSmallMaxGroups][2], xl[kSmallMaxGroups][2];
+    uint16_t wsc[kSmallMaxGroups], xsc[kSmallMaxGroups];
+#pragma unroll
+    for (int i = 0; i < kSmallMaxGroups; ++i) {
+      if (i < ng) {
+        const int g = ga + i;
+        wl[i][0] = *reinterpret_cast<const uint4*>(wrow + (size_t)g * 64);
+        wl[i][1] = *reinterpret_cast<const uint4*>(wrow + (size_t)g * 64 + 16);
+        xl[i][0] = *reinterpret_cast<const uint4*>(xrow + (size_t)g * 64);
+        xl[i][1] = *reinterpret_cast<const uint4*>(xrow + (size_t)g * 64 + 16);
+        wsc[i] = sw[(size_t)g * N + n];
+        xsc[i] = sx[(size_t)g * M + m];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kSmallMaxGroups; ++i) {
+      if (i < ng) {
+        const v8i a = decode32(wl[i][0], wl[i][1], rot);
+        const v8i b = decode32(xl[i][0], xl[i][1], rot);
+        const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{}, 0, 0, 0, kScaleE8M0, 0, kScaleE8M0);
+        const v4f sp = __builtin_amdgcn_mfma_f32_16x16x16f16(scale_operand(wsc[i]), scale_operand(xsc[i]), v4f{}, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yacc[j] = __builtin_fmaf(acc[j], sp[j], yacc[j]);
+      }
+    }
+    if (range == ranges - 1) {   // INT8 outlier group: 16-byte K slice of each 64-byte half
+      const size_t o = rb - ATOM_OUTLIERS + 16 * slice;
+      v4i w8[2], x8[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        w8[c] = *reinterpret_cast<const v4i*>(Wq + (size_t)n * rb + o + 64 * c);
+        x8[c] = *reinterpret_cast<const v4i*>(Xq + (size_t)m * rb + o + 64 * c);
+      }
+      const uint16_t wsc8 = sw[(size_t)(G - 1) * N + n], xsc8 = sx[(size_t)(G - 1) * M + m];
+      v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8[0], x8[0], v4i{}, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8[1], x8[1], acc, 0, 0, 0);
+      const v4f sp = __builtin_amdgcn_mfma_f32_16x16x16f16(scale_operand(wsc8), scale_operand(xsc8), v4f{}, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) yacc[j] = __builtin_fmaf((float)acc[j], sp[j], yacc[j]);   // |acc| < 2^24: exact
+    }
+  }
+
+  red[wave][lane] = yacc;
+  __syncthreads();
+  if (wave != 0) return;
+  v4f y = red[0][lane];
+  for (int w = 1; w < waves; ++w) {
+    const v4f v = red[w][lane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] += v[j];
+  }
+  // lane: token row r, columns n0 + 4 slice .. + 3; the factor 4 of the scale products goes
+  if (r >= M) return;
+  const int c0 = n0 + 4 * slice;
+  uint16_t* dst = Y + (size_t)r * N + c0;
+  const uint16_t o[4] = {__half_as_ushort(__float2half_rn(0.25f * y[0])), __half_as_ushort(__float2half_rn(0.25f * y[1])),
+                         __half_as_ushort(__float2half_rn(0.25f * y[2])), __half_as_ushort(__float2half_rn(0.25f * y[3]))};
+  if (c0 + 4 <= N && (N & 3) == 0) {
+    *reinterpret_cast<ushort4*>(dst) = ushort4{o[0], o[1], o[2], o[3]};
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (c0 + j < N) dst[j] = o[j];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_small(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M,
+                             int N, int K, uint16_t* Y, hipStream_t stream) {
+  const int G = K / ATOM_GROUP;
+  const int ranges = (G - 1 + kSmallMaxGroups - 1) / kSmallMaxGroups;
+  const int waves = ranges < kMaxWaves ? ranges : kMaxWaves;
+  hipLaunchKernelGGL(gemm_w4a4_small_kernel, dim3((N + kCols - 1) / kCols), dim3(64 * waves), 0, stream, Xq, sx, Wq,
+                     sw, M, N, K, ranges, Y);
+  return hipGetLastError();
+}
+
+}  // namespace atom

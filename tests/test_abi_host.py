@@ -156,7 +156,10 @@ def test_gemm_workspace_query(lib):
     # 256 x 4096 output = 2 x 32 tiles: every tile split four ways
     assert bq.atom_gemm_workspace_bytes(256, 4096, 4096) == 64 * 4 * T
     assert bq.atom_gemm_workspace_bytes(64, 128, 4096) == 1 * 7 * T       # capped by 31 INT4 groups / 4
-    assert bq.atom_gemm_workspace_bytes(1, 130, 1152) == 2 * 2 * T
+    # M <= 16: the few-rows kernel reduces its K ranges inside the workgroup: no scratch
+    for M, N, K in [(1, 130, 1152), (1, 4096, 4096), (16, 4096, 11008), (3, 131, 2048), (16, 16, 32768)]:
+        assert bq.atom_gemm_workspace_bytes(M, N, K) == 0
+    assert bq.atom_gemm_workspace_bytes(17, 128, 4096) == 1 * 7 * T        # 17 rows: 128 x 128 tiles, split-K
     assert bq.atom_gemm_workspace_bytes(127 * 128, 128, 256 * 128) == 127 * 3 * T   # ceil(256 / 127) = 3
     # 128 tiles or more, or too few groups to divide: no scratch
     assert bq.atom_gemm_workspace_bytes(128 * 128, 128, 4096) == 0

@@ -275,7 +275,7 @@ def test_deterministic_and_side_stream():
 
 
 # --------------------------------------------------------------------------- split-K (atom_gemm_ws)
-SPLIT = [(64, 128, 4096), (200, 300, 2048), (1, 130, 1152), (256, 4096, 4096)]
+SPLIT = [(64, 128, 4096), (200, 300, 2048), (17, 130, 1152), (256, 4096, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", SPLIT)
@@ -310,3 +310,28 @@ def test_gemm_ws_without_enough_scratch_is_atom_gemm():
         y = host(bq.atom_gemm_ws(Xq, sx, Wq, sw, K, ws))
         np.testing.assert_array_equal(y.view(np.uint16), ref.view(np.uint16))
 
+
+
+# --------------------------------------------------------------------------- few rows (M <= 16)
+SMALL = [(1, 4096, 4096), (16, 11008, 4096), (16, 4096, 11008), (3, 131, 2048), (7, 37, 256), (16, 16, 1152),
+         (5, 200, 32768), (12, 1000, 1408)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_gemm_small_m_matches_oracle(M, N, K):
+    """M <= 16 runs the few-rows kernel (K ranges of at most 4 INT4 groups, one wave each, added
+    in LDS): Y against the oracle on up to 512 sampled columns (all of them for small N), and
+    bit-identical on a second call and through atom_gemm_ws."""
+    _say(f"[few rows] M={M} N={N} K={K}")
+    assert bq.atom_gemm_workspace_bytes(M, N, K) == 0
+    x, wt, _ = synth.make_linear(M, K, N, seed=M * 131 + N + K)
+    perm = np.random.default_rng(K + 3).permutation(K).astype(np.int32)
+    Xq, sx = bq.atom_quantize_act(dev(x), dev(perm))
+    Wq, sw = bq.atom_pack_weights(dev(wt), dev(perm))
+    Y = host(bq.atom_gemm(Xq, sx, Wq, sw, K))
+    cols = np.arange(N) if N <= 512 else np.sort(np.random.default_rng(9).choice(N, 512, replace=False))
+    qx, sxr = O.quantize_rows(x, perm)
+    qw, swr = O.quantize_rows(wt[cols], perm)
+    assert_y_close(Y[:, cols], O.gemm_ref(qx, sxr, qw, swr), f"few rows {M}x{N}x{K}")
+    for y2 in (bq.atom_gemm(Xq, sx, Wq, sw, K), bq.atom_gemm_ws(Xq, sx, Wq, sw, K, None)):
+        np.testing.assert_array_equal(Y.view(np.uint16), host(y2).view(np.uint16))
