@@ -38,6 +38,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
 WORKLOAD_SETS = {
     "llama7b": ["A", "B", "C"],
     "A": ["A"], "B": ["B"], "C": ["C"], "D": ["D"],
+    # 16 tokens through the same weights: the few-rows GEMM, bound by reading the packed weights
+    "decode": ["dA", "dB", "dC"],
     "Dq": [],              # activation quantize alone on 8192 x 8192 fp16 (128 outlier channels x30)
 }
 
@@ -282,6 +284,8 @@ def main():
     gemm_ops = sum(s["w"].ops for s in sets)
     gemm_us = sum(per[s["key"]]["gemm_us"] for s in sets)
     gemm_tops = gemm_ops / (gemm_us * 1e-6) / 1e12
+    gemm_bytes_step = sum(gemm_bytes(s["w"].M, s["w"].N, s["w"].K) for s in sets)
+    gemm_gbs = gemm_bytes_step / (gemm_us * 1e-6) / 1e9
     shapes = {}
     for s in sets:
         w = s["w"]
@@ -329,6 +333,12 @@ def main():
             "kernel": "gemm_w4a4_kernel", "bound": "mfma", "achieved": round(gemm_tops, 1),
             "peak": round(INT8_PEAK_TOPS, 1), "unit": "TOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
             "traffic": traffic, "ops_per_launch": gemm_ops / len(sets),
+            "avg_launch_us": round(gemm_us / len(sets), 3),
+        } if args.workload != "decode" else {
+            # few rows: every weight byte is used at most 16 times, so the bound is HBM
+            "kernel": "gemm_w4a4_small_kernel", "bound": "hbm", "achieved": round(gemm_gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None, "bytes_per_launch": gemm_bytes_step / len(sets),
             "avg_launch_us": round(gemm_us / len(sets), 3),
         },
         "shapes": shapes,

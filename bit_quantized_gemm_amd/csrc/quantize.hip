@@ -88,10 +88,15 @@ __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, ui
 // CHUNKS: 16-byte row chunks each thread prefetches (K <= CHUNKS * 2048).
 // PASSES: passes of 4096 reordered elements per row whose gather offsets stay in registers
 // for the whole kernel (K <= PASSES * 4096); 0 = read perm from memory on every row.
+// Work items: split == 1: item = one row, all passes; split == PASSES: item = one pass of one
+// row (item / split = row, item % split = pass), used when there are fewer rows than resident
+// workgroups, so that a short batch still spreads over the chip (each item stages the whole
+// row, which an arbitrary reorder needs; the repeated row reads hit in L2).
 template <int CHUNKS, int PASSES>
 __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* __restrict__ X,
                                                                 const int32_t* __restrict__ perm, int rows, int K,
-                                                                uint8_t* __restrict__ Q, uint16_t* __restrict__ S) {
+                                                                int split, uint8_t* __restrict__ Q,
+                                                                uint16_t* __restrict__ S) {
   extern __shared__ uint32_t lds_words[];
   const uint8_t* lds_bytes = reinterpret_cast<const uint8_t*>(lds_words);
   const int QP = staged_stride(K);
@@ -189,9 +194,11 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
     if ((threadIdx.x & (kLanesPerGroup - 1)) == 0) S[(size_t)g * rows + row] = __half_as_ushort(s16);
   };
 
-  int row = blockIdx.x;
-  if (row < rows) prefetch(row);
-  for (; row < rows; row += gridDim.x) {
+  const int items = rows * split;
+  int item = blockIdx.x;
+  if (item < items) prefetch(item / split);
+  for (; item < items; item += gridDim.x) {
+    const int row = item / split, part = item - row * split;
     __syncthreads();                                 // everyone finished reading the previous row
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
@@ -206,14 +213,14 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
       }
     }
     __syncthreads();
-    if (row + (int)gridDim.x < rows) prefetch(row + gridDim.x);   // next row's loads fly meanwhile
+    if (item + (int)gridDim.x < items) prefetch((item + gridDim.x) / split);   // next item's loads fly meanwhile
 
     uint8_t* qrow = Q + (size_t)row * rb;
     if (PASSES > 0) {
 #pragma unroll
       for (int ps = 0; ps < (PASSES > 0 ? PASSES : 1); ++ps) {
         const int c = threadIdx.x * kPerThread + ps * kPassElems;
-        if (c < K) quantize16(c, offs[ps], qrow, row);
+        if (c < K && (split == 1 || ps == part)) quantize16(c, offs[ps], qrow, row);
       }
     } else {
       for (int c = threadIdx.x * kPerThread; c < K; c += kPassElems) {
@@ -242,9 +249,13 @@ hipError_t launch_rq(const uint16_t* X, const int32_t* perm, int rows, int K, ui
     if (per_cu <= 0) per_cu = 2;
   }
   const int lim = per_cu * cus;
-  const int grid = rows < lim ? rows : lim;         // persistent: one wave of workgroups
+  // passes of a row as separate items when the rows alone leave resident slots empty
+  const int passes = (K + kThreads * kPerThread - 1) / (kThreads * kPerThread);
+  const int split = (PASSES > 1 && rows < lim) ? passes : 1;
+  const long long items = (long long)rows * split;
+  const int grid = items < lim ? (int)items : lim;   // persistent: one wave of workgroups
   hipLaunchKernelGGL((row_quantize_kernel<CHUNKS, PASSES>), dim3(grid), dim3(kThreads), lds, stream, X, perm, rows,
-                     K, Q, S);
+                     K, split, Q, S);
   return hipGetLastError();
 }
 

@@ -49,6 +49,11 @@ WORKLOADS: dict[str, Workload] = {
         Workload("B", "llama7b_mlp_gate_up_1024x4096x11008", 1024, 4096, 11008, "outliers", 128, 20.0, 0.02),
         Workload("C", "llama7b_mlp_down_2048x11008x4096", 2048, 11008, 4096, "silu", 0, 1.0, 0.015),
         Workload("D", "llama70b_mlp_4096x8192x28672", 4096, 8192, 28672, "rows_of_quant", 128, 30.0, 0.02),
+        # decode-sized batches (16 tokens) through the same three Llama-7B weight shapes
+        Workload("dA", "llama7b_attn_proj_decode_16x4096x4096", 16, 4096, 4096, "laplace",
+                 int(round(0.01 * 4096)), 25.0, 0.02),
+        Workload("dB", "llama7b_mlp_gate_up_decode_16x4096x11008", 16, 4096, 11008, "outliers", 128, 20.0, 0.02),
+        Workload("dC", "llama7b_mlp_down_decode_16x11008x4096", 16, 11008, 4096, "silu", 0, 1.0, 0.015),
     ]
 }
 
