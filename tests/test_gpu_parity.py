@@ -335,3 +335,53 @@ def test_gemm_small_m_matches_oracle(M, N, K):
     assert_y_close(Y[:, cols], O.gemm_ref(qx, sxr, qw, swr), f"few rows {M}x{N}x{K}")
     for y2 in (bq.atom_gemm(Xq, sx, Wq, sw, K), bq.atom_gemm_ws(Xq, sx, Wq, sw, K, None)):
         np.testing.assert_array_equal(Y.view(np.uint16), host(y2).view(np.uint16))
+
+
+# --------------------------------------------------------------------------- HIP graph capture
+def test_graph_capture_replays_match_eager():
+    """The library allocates and synchronizes nothing, so quantize + GEMM can be captured in a
+    HIP graph.  Three shapes cover the three GEMM paths (split-K with its finalize kernel, whole
+    128 x 128 tiles, few rows); the graph is replayed several times with unrelated eager work
+    and new inputs in between, and every replay must equal the eager result bit for bit."""
+    cases = [(256, 4096, 4096), (1024, 2048, 1024), (16, 2000, 11008)]
+    st = torch.cuda.Stream()
+    bufs = []
+    for i, (M, N, K) in enumerate(cases):
+        x, wt, _ = synth.make_linear(M, K, N, seed=40 + i)
+        perm = dev(np.random.default_rng(i).permutation(K).astype(np.int32))
+        Wq, sw = bq.atom_pack_weights(dev(wt), perm)
+        need = bq.atom_gemm_workspace_bytes(M, N, K)
+        b = dict(K=K, X=dev(x), perm=perm, Wq=Wq, sw=sw,
+                 Xq=torch.empty((M, bq.atom_row_bytes(K)), dtype=torch.uint8, device="cuda"),
+                 sx=torch.empty((K // 128, M), dtype=torch.float16, device="cuda"),
+                 Y=torch.empty((M, N), dtype=torch.float16, device="cuda"),
+                 ws=torch.empty(need, dtype=torch.uint8, device="cuda") if need else None)
+        bufs.append(b)
+
+    def step():
+        for b in bufs:
+            bq.atom_quantize_act(b["X"], b["perm"], Xq=b["Xq"], sx=b["sx"], stream=st)
+            bq.atom_gemm_ws(b["Xq"], b["sx"], b["Wq"], b["sw"], b["K"], b["ws"], Y=b["Y"], stream=st)
+
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        step()                                   # warm up (first-use queries happen outside capture)
+    st.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for b in bufs:                           # new activations each replay, plus eager noise
+            b["X"].mul_(-1.0 if rep % 2 else 1.0)
+            torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host(b["Y"]).copy() for b in bufs]
+        with torch.cuda.stream(st):
+            step()                               # eager on the same inputs
+        st.synchronize()
+        for i, b in enumerate(bufs):
+            np.testing.assert_array_equal(got[i].view(np.uint16), host(b["Y"]).view(np.uint16),
+                                          err_msg=f"replay {rep}, shape {cases[i]}")
