@@ -24,6 +24,14 @@ bool valid_k(int32_t K) { return K >= 2 * ATOM_GROUP && K <= ATOM_MAX_K && K % A
 
 bool valid_rows(int32_t r) { return r >= 1 && r <= ATOM_MAX_ROWS; }
 
+// GEMM shapes: both row counts valid and the 128 x 128 output tiles (a 1-D grid, with split-K
+// pieces on top) well inside the 32-bit grid range.
+bool valid_gemm(int32_t M, int32_t N, int32_t K) {
+  if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return false;
+  const uint64_t tiles = (uint64_t)((M + 127) / 128) * (uint64_t)((N + 127) / 128);
+  return tiles <= ATOM_MAX_TILES;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? ATOM_OK : ATOM_E_HIP; }
 
 // Every output must be disjoint from every input and from the other outputs.
@@ -110,14 +118,14 @@ int atom_quantize_act(const void* X, const int32_t* perm, int32_t M, int32_t K, 
 }
 
 int64_t atom_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
-  if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return -(int64_t)ATOM_E_SHAPE;
+  if (!valid_gemm(M, N, K)) return -(int64_t)ATOM_E_SHAPE;
   return atom::gemm_workspace_bytes(atom::gemm_plan(M, N, K), M, N);
 }
 
 int atom_gemm_ws(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N, int32_t K,
                  void* Y, void* workspace, int64_t workspace_bytes, void* stream) {
   if (!Xq || !sx || !Wq || !sw || !Y) return ATOM_E_NULL;
-  if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return ATOM_E_SHAPE;
+  if (!valid_gemm(M, N, K)) return ATOM_E_SHAPE;
   if (!aligned16(Xq) || !aligned16(sx) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y)) return ATOM_E_ALIGN;
   atom::GemmPlan plan = atom::gemm_plan(M, N, K);
   int64_t need = atom::gemm_workspace_bytes(plan, M, N);
@@ -147,7 +155,7 @@ int atom_gemm(const void* Xq, const void* sx, const void* Wq, const void* sw, in
 int atom_gemm_group_acc(const void* Xq, const void* Wq, int32_t M, int32_t N, int32_t K, int32_t* acc,
                         void* stream) {
   if (!Xq || !Wq || !acc) return ATOM_E_NULL;
-  if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return ATOM_E_SHAPE;
+  if (!valid_gemm(M, N, K)) return ATOM_E_SHAPE;
   if (!aligned16(Xq) || !aligned16(Wq) || !aligned16(acc)) return ATOM_E_ALIGN;
   const uint64_t G = (uint64_t)K / ATOM_GROUP;
   const uint64_t rb = (uint64_t)atom_row_bytes(K);

@@ -46,11 +46,13 @@ extern "C" {
 #define ATOM_OUTLIERS 128     /* high-precision outlier channels (record, "notes") */
 #define ATOM_MAX_K 32768      /* largest K the kernels stage in LDS */
 #define ATOM_MAX_ROWS (1 << 24)
+#define ATOM_MAX_TILES (1 << 26) /* GEMM: ceil(M/128) * ceil(N/128) output tiles at most */
 
 enum {
   ATOM_OK = 0,
   ATOM_E_NULL = 1,     /* a required pointer is NULL */
-  ATOM_E_SHAPE = 2,    /* K not a multiple of 128, K < 256 or > ATOM_MAX_K, rows out of range */
+  ATOM_E_SHAPE = 2,    /* K not a multiple of 128, K < 256 or > ATOM_MAX_K, rows out of range,
+                          GEMM with more than ATOM_MAX_TILES output tiles */
   ATOM_E_ALIGN = 3,    /* a pointer is not 16-byte aligned */
   ATOM_E_OVERLAP = 4,  /* an output range overlaps an input or another output range */
   ATOM_E_HIP = 5       /* the HIP runtime reported an error when enqueuing */

@@ -44,6 +44,7 @@ def test_header_constants():
     assert re.search(r"#define ATOM_GROUP 128\b", text)
     assert re.search(r"#define ATOM_OUTLIERS 128\b", text)
     assert re.search(rf"#define ATOM_MAX_K {bq.MAX_K}\b", text)
+    assert re.search(r"#define ATOM_MAX_TILES \(1 << 26\)", text)
 
 
 def test_shape_helpers(lib):
@@ -171,6 +172,17 @@ def test_gemm_workspace_query(lib):
     assert lib.atom_gemm_workspace_bytes(0, 4, 256) == -E_SHAPE
     with pytest.raises(bq.AtomError):
         bq.atom_gemm_workspace_bytes(4, 4, 200)
+
+
+def test_gemm_tile_limit(lib):
+    # 2^24 x 2^24 output: 2^34 tiles of 128 x 128 -- rejected before anything is launched
+    big = 1 << 24
+    assert lib.atom_gemm(A, B, C, D, big, big, 256, E, S) == E_SHAPE
+    assert lib.atom_gemm_ws(A, B, C, D, big, big, 256, E, None, 0, S) == E_SHAPE
+    assert lib.atom_gemm_group_acc(A, C, big, big, 256, E, S) == E_SHAPE
+    assert lib.atom_gemm_workspace_bytes(big, big, 256) == -E_SHAPE
+    # 2^13 x 2^13 tile grid = 2^26 tiles: the largest accepted
+    assert lib.atom_gemm_workspace_bytes(1 << 20, 1 << 20, 256) == 0
 
 
 def test_gemm_ws_validation(lib):
