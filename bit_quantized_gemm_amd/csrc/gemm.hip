@@ -24,20 +24,19 @@
 // single fp32 FMA; the factor 2 is removed once at the store.
 //
 // Pipeline.  A packed row is a sequence of 64-byte stages: stage s < G-1 is INT4 group s,
-// stages G-1 and G are the two 64-byte halves of the INT8 outlier group.  Each thread loads
-// its 16-byte chunks of a stage of the A (activation) and B (weight) tiles with buffer loads
-// (the stage offset is a scalar) and copies them, still packed, to LDS (double-buffered).
-// Every wave reads the packed bytes of its own operands and decodes them in registers just
-// before the MFMAs that use them, so LDS carries 64 bytes per row and group (its write rate
-// is the scarce one) and the decode runs under the matrix core.  While group s is
-// multiplied, stage s+1 is written to LDS and the loads of stage s+2 are in flight; one
-// barrier per stage, placed before the last epilogues of group s so that the operand reads
-// of group s+1 overlap them.
+// stages G-1 and G are the two 64-byte halves of the INT8 outlier group.  Each wave copies
+// 16-row slabs of a stage of the A (activation) and B (weight) tiles straight into LDS with
+// LDS-DMA buffer loads (16 bytes per lane, the stage offset in a scalar), still packed, so
+// LDS carries 64 bytes per row and group and no registers or VALU work go into staging.
+// Three stage buffers form a ring: while group s is multiplied its operands are in
+// registers, stage s+1 has landed and is read into registers as they free up, and stages
+// s+2 and s+3 are in flight.  One barrier per group.  Every wave decodes the packed bytes of
+// its own operands in registers just before the MFMAs that use them.
 //
 // LDS layout.  A staged row is 64 bytes = four 16-byte chunks; chunk c of row r is stored at
-// position c ^ ((r >> 2) & 3).  The 16 lanes of a ds_read_b128 group (16 consecutive rows,
-// one chunk) and those of a ds_write_b128 group (4 rows x 4 chunks) each cover all 16 bank
-// groups of 16 bytes.
+// position c ^ ((r >> 2) & 3), so the 16 lanes of a ds_read_b128 group (16 consecutive rows,
+// one chunk) cover all 16 bank groups of 16 bytes.  A copy writes 16 consecutive bytes per
+// lane, so the swizzle is applied to the global address each lane copies from.
 //
 // Waves.  A workgroup of WAVES_M x WAVES_N waves computes a BM x BN tile of Y; each wave
 // owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile held as 32x32 MFMA tiles.  Lane l supplies row
@@ -55,7 +54,6 @@ typedef int32_t v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int32_t v8i __attribute__((ext_vector_type(8)));
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // native vector: stays in VGPRs
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStageBytes = 64;          // bytes of one stage of a packed row
