@@ -10,6 +10,13 @@
 
 namespace atom {
 
+// Packed INT4 unit (16 codes, 8 bytes; written by the row quantize, read by the GEMMs): the
+// codes' fp6 e2m3 fields (c / 8 as a subnormal: |c| in bits 0-2, sign in bit 5) at bits 6i of
+// a 96-bit string T0:T1:T2, stored as T0 | (T2 & kFp6Exp0), T1 | (T2 & kFp6Exp1).  The masks
+// are the exponent bits (3 and 4 of each field) of T0 and T1, always zero for INT4 codes;
+// T2's nonzero bits are exactly their union, so T2 = (w0 & kFp6Exp0) | (w1 & kFp6Exp1).
+constexpr uint32_t kFp6Exp0 = 0x18618618u, kFp6Exp1 = 0x86186186u;
+
 hipError_t launch_channel_stat(const uint16_t* X, int M, int K, double* stat, hipStream_t stream);
 hipError_t launch_select_outliers(const double* stat, int K, int32_t* perm, hipStream_t stream);
 hipError_t launch_row_quantize(const uint16_t* X, const int32_t* perm, int rows, int K, uint8_t* Q,

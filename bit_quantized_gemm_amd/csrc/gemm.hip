@@ -6,13 +6,13 @@
 // LLM Serving", Abstract; quantization record, "notes": an integer-operator path, not FP4).
 //
 // INT4 groups.  gfx950 has no 4-bit integer MFMA.  An INT4 code q in [-7, 7] is exactly the
-// fp8 e4m3 subnormal with bits (q < 0) << 7 | |q| (value q * 2^-9), and the packed
-// sign-magnitude layout turns a 32-bit word of eight codes into four such bytes with one AND
-// (even codes: w & 0x87878787) or one rotate and one AND (odd codes: rotr(w, 4) & 0x87878787).
-// v_mfma_scale_f32_32x32x64_f8f6f4 with unit-exponent scales 2^9 * 2^9 then returns the
-// group's integer dot product exactly in fp32: every product and partial sum is an integer
-// of magnitude below 2^24.  The INT4 groups thus run at the dense fp8 rate (equal to the int8
-// rate) and their accumulators are already fp32.
+// fp6 e2m3 subnormal with bits (q < 0) << 5 | |q| (value q / 8), and the packed layout (a unit
+// of 16 codes = the 96 bits of their fp6 fields with the third word folded into the always-zero
+// exponent bits of the first two, see atom_internal.h) turns 8 bytes into 12 operand bytes
+// with four bit operations.  v_mfma_scale_f32_32x32x64_f8f6f4 on fp6 operands with scales
+// 2^3 * 2^3 then returns the group's integer dot product exactly in fp32: every product and
+// partial sum is an integer of magnitude below 2^24.  The INT4 groups thus run at the dense
+// fp6 rate, twice the int8 / fp8 rate, and their accumulators are already fp32.
 //
 // INT8 outlier group (record, "notes": a 128-channel high-precision group): int8 codes feed
 // v_mfma_i32_32x32x32_i8 directly; its int32 accumulators are converted once.
@@ -21,7 +21,8 @@
 // v_mfma_f32_32x32x8_f16 whose only nonzero K slots (0 and 4) hold the fp16 scales: fp16 x
 // fp16 is exact in fp32, the two equal products sum exactly to 2 * sx * sw, and the result
 // lands in the accumulator layout.  The epilogue per output element and group is then a
-// single fp32 FMA; the factor 2 is removed once at the store.
+// single fp32 FMA; the factor 2 is removed once at the store.  Each thread stores its fp16
+// scale in LDS as a ready 8-byte operand (scale, 0, 0, 0), read with one ds_read_b64.
 //
 // Pipeline.  A packed row is a sequence of 64-byte stages: stage s < G-1 is INT4 group s,
 // stages G-1 and G are the two 64-byte halves of the INT8 outlier group.  Each wave copies
@@ -60,20 +61,22 @@ constexpr int kStageBytes = 64;          // bytes of one stage of a packed row
 constexpr int kLdsRow = 64;              // bytes of one staged (packed) row in LDS
 constexpr int kXcds = 8;                 // accelerator complex dies (each with its own L2)
 constexpr int kBandM = 8;                // tile rows per band of the tile order
-constexpr int kScaleE8M0 = 127 + 9;      // 2^9: the e4m3 subnormal q * 2^-9 counts as q
+constexpr int kScaleE8M0 = 127 + 3;      // 2^3: the e2m3 subnormal q / 8 counts as q
 
-__device__ __forceinline__ uint32_t rotr4(uint32_t w) { return __builtin_amdgcn_alignbit(w, w, 4); }
-
-constexpr uint32_t kFp8Mask = 0x87878787u;   // sign bit and 3-bit magnitude of each byte
-
-// fp8 e4m3 operands of 32 packed INT4 codes pairs: even codes (w & mask) and odd codes
-// (rotr(w, 4) & mask) of each 32-bit word
-__device__ __forceinline__ v8i fp8_even(v8i w) { return w & (int)kFp8Mask; }
-
-__device__ __forceinline__ v8i fp8_odd(v8i w) {
+// fp6 operand (32 codes, six words) of the two packed units in words 4h .. 4h+3 of w: unit
+// words (w0, w1) -> fields T0 = w0 & ~kFp6Exp0, T1 = w1 & ~kFp6Exp1,
+// T2 = (w0 & kFp6Exp0) | (w1 & kFp6Exp1).  The last two words are not read by the fp6 MFMA.
+__device__ __forceinline__ v8i fp6_operand(v8i w, int h) {
   v8i r;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) r[k] = (int)(rotr4((uint32_t)w[k]) & kFp8Mask);
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t w0 = (uint32_t)w[4 * h + 2 * u], w1 = (uint32_t)w[4 * h + 2 * u + 1];
+    r[3 * u] = (int)(w0 & ~kFp6Exp0);
+    r[3 * u + 1] = (int)(w1 & ~kFp6Exp1);
+    r[3 * u + 2] = (int)((w0 & kFp6Exp0) | (w1 & kFp6Exp1));
+  }
+  r[6] = 0;
+  r[7] = 0;
   return r;
 }
 
@@ -82,9 +85,9 @@ __device__ __forceinline__ v8i fp8_odd(v8i w) {
 // transposed: lane l owns output row l & 31, and its element r is column
 // (r >> 2) * 8 + (l >> 5) * 4 + (r & 3), i.e. four runs of four consecutive columns that
 // the epilogue stores as vectors.
-__device__ __forceinline__ v16f mma_fp8(v8i a, v8i b, v16f c) {
-  // cbsz = blgp = 0: both operands fp8 e4m3; opsel 0 and E8M0 scale 2^9 on both sides
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, kScaleE8M0, 0, kScaleE8M0);
+__device__ __forceinline__ v16f mma_fp6(v8i a, v8i b, v16f c) {
+  // cbsz = blgp = 2: both operands fp6 e2m3; opsel 0 and E8M0 scale 2^3 on both sides
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 2, 2, 0, kScaleE8M0, 0, kScaleE8M0);
 }
 
 __device__ __forceinline__ v16i mma_i8(v4i a, v4i b, v16i c) {
@@ -199,10 +202,10 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   // does not write what is read from another, and waits only where a buffer is really shared.
   __shared__ __attribute__((aligned(16))) uint8_t la0[BM * kLdsRow], la1[BM * kLdsRow], la2[BM * kLdsRow];
   __shared__ __attribute__((aligned(16))) uint8_t lb0[BN * kLdsRow], lb1[BN * kLdsRow], lb2[BN * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t ls0[BM + BN], ls1[BM + BN], ls2[BM + BN];   // sx rows, then sw
+  __shared__ __attribute__((aligned(16))) h4 ls0[BM + BN], ls1[BM + BN], ls2[BM + BN];   // sx rows, then sw
   auto LA = [&](int p) -> uint8_t* { return p == 0 ? la0 : p == 1 ? la1 : la2; };
   auto LB = [&](int p) -> uint8_t* { return p == 0 ? lb0 : p == 1 ? lb1 : lb2; };
-  auto LS = [&](int p) -> uint16_t* { return p == 0 ? ls0 : p == 1 ? ls1 : ls2; };
+  auto LS = [&](int p) -> h4* { return p == 0 ? ls0 : p == 1 ? ls1 : ls2; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -280,18 +283,16 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   // Rank-one fp16 scale operands of a group: every lane puts its row's sx (A) / column's sw
   // (B) in K slot 0 of its half, so the f16 MFMA returns 2 * sx * sw exactly (two equal
   // exact products).  Every term of the Y accumulators thus carries the factor 2, which the
-  // final store removes; a power of two changes no rounding.
-  auto read_scales = [&](const uint16_t* ls, h4 (&sa)[T::kTM], h4 (&sb)[T::kTN]) {
+  // final store removes; a power of two changes no rounding.  LDS holds each scale already
+  // as its operand (scale, 0, 0, 0).
+  auto scale_operand = [](uint16_t v) {
+    return h4{__builtin_bit_cast(_Float16, v), (_Float16)0, (_Float16)0, (_Float16)0};
+  };
+  auto read_scales = [&](const h4* ls, h4 (&sa)[T::kTM], h4 (&sb)[T::kTN]) {
 #pragma unroll
-    for (int i = 0; i < T::kTM; ++i) {
-      const uint16_t v = ls[wm * T::kWTM + i * 32 + l32];
-      sa[i] = h4{__builtin_bit_cast(_Float16, v), (_Float16)0, (_Float16)0, (_Float16)0};
-    }
+    for (int i = 0; i < T::kTM; ++i) sa[i] = ls[wm * T::kWTM + i * 32 + l32];
 #pragma unroll
-    for (int j = 0; j < T::kTN; ++j) {
-      const uint16_t v = ls[BM + wn * T::kWTN + j * 32 + l32];
-      sb[j] = h4{__builtin_bit_cast(_Float16, v), (_Float16)0, (_Float16)0, (_Float16)0};
-    }
+    for (int j = 0; j < T::kTN; ++j) sb[j] = ls[BM + wn * T::kWTN + j * 32 + l32];
   };
 
   // Rank-one scale product 2 * sx (x) sw of tile (i, j), in the accumulator layout.
@@ -318,8 +319,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
 
   // This wave's packed operand bytes of one stage: for tile row i (A) / column j (B), the
   // lane's row, chunks 2kh and 2kh+1 (stage bytes 32kh .. 32kh+31).  On an INT4 stage these
-  // are 64 codes whose even and odd halves are the lane's K=32 slices of the two K=64 fp8
-  // operands; on an INT8 stage, its K slices of two K=32 int8 operands.
+  // are four units of 16 codes: chunk 2kh is the lane's K=32 slice of the first K=64 fp6
+  // operand, chunk 2kh+1 of the second; on an INT8 stage, its K slices of two K=32 int8
+  // operands.
   auto read_a = [&](const uint8_t* la, int i) {
     return cat(lds_chunk(la, a_row, i, 2 * kh), lds_chunk(la, a_row, i, 2 * kh + 1));
   };
@@ -358,9 +360,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
     __builtin_amdgcn_sched_barrier(0);
     if (!kAcc) {
       sreg = load_scale(ad, ga + 3, G, M, N);
-      ls0[tid] = s0;
-      ls1[tid] = s1;
-      ls2[tid] = s2;
+      ls0[tid] = scale_operand(s0);
+      ls1[tid] = scale_operand(s1);
+      ls2[tid] = scale_operand(s2);
     }
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kPerStage));   // stages ga and ga+1 have landed
     wg_barrier();
@@ -374,53 +376,51 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
 
   // INT4 group s in ring position P (stage s in buffer P).  A wave issues in order, so nothing
   // may wait on the MFMA issued just before it.  Per tile row i: region a decodes A row i
-  // (and every B column at i = 0), reads the matching operands of stage s+1, applies tile
-  // (i-1, 0) (at i = 0: tile (kTM-1, 1) of group s-1, carried over), issues the scale product
-  // of tile (i, 0) and the even-code MFMAs of tiles (i, 0) and (i, 1); region b applies tile
-  // (i-1, 1), issues the scale product of tile (i, 1) and the odd-code MFMAs of both tiles,
-  // each after an independent MFMA.  A tile's sums (two K=64 fp8 MFMAs: the exact group sum
-  // in fp32) and its scale product are complete when they are applied.  The scheduling
-  // fences keep this order.
+  // (and every B column at i = 0), reads the matching operands of stage s+1, issues the scale
+  // product and the two K=64 fp6 MFMAs of tile (i, 0), then applies tile (i-1, 1); region b
+  // issues the scale product and MFMAs of tile (i, 1), then applies tile (i, 0).  Each apply
+  // thus comes after three MFMAs that do not feed it, so a tile's sums (the exact group sum
+  // in fp32) and its scale product are complete when they are used, and no more than two
+  // tiles' sums and scale products are live at a time.  The scheduling fences keep this order.
   static_assert(T::kTN == 2, "tile rows are processed as pairs of 32x32 tiles");
   auto int4_group = [&](auto ring, int s) {
     constexpr int p = decltype(ring)::kCur, pn = decltype(ring)::kNext;
     // refill buffer p (stage s was read during group s-1, before the last barrier)
     if (!kAcc) {
-      LS(p)[tid] = sreg;
+      LS(p)[tid] = scale_operand(sreg);
       sreg = load_scale(ad, s + 4, G, M, N);
     }
     __builtin_amdgcn_sched_barrier(0);
     dma_stage(ad, LA(p), LB(p), min(s + 3, G));               // past the row end: unused
     __builtin_amdgcn_sched_barrier(0);
-    v16f acc[T::kTM][2], sp[T::kTM][2];
-    v8i be[2], bo[2];
+    v16f acc0, sp0, acc1, sp1;                                 // tiles (i, 0) and (i, 1)
+    v8i b0[2], b1[2];                                          // fp6 operands of the B columns
     h4 san[T::kTM], sbn[T::kTN];
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i) {
-      const v8i ae = fp8_even(pa[i]), ao = fp8_odd(pa[i]);
+      const v8i a0 = fp6_operand(pa[i], 0), a1 = fp6_operand(pa[i], 1);
       if (i == 0) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          be[j] = fp8_even(pb[j]);
-          bo[j] = fp8_odd(pb[j]);
+          b0[j] = fp6_operand(pb[j], 0);
+          b1[j] = fp6_operand(pb[j], 1);
           pb[j] = read_b(LB(pn), j);
         }
         if (!kAcc) read_scales(LS(pn), san, sbn);
       }
       pa[i] = read_a(LA(pn), i);
-      if (i > 0) apply(i - 1, 0, acc[i - 1][0], sp[i - 1][0], s);
-      sp[i][0] = scale_product(sa[i], sb[0]);
-      acc[i][0] = mma_fp8(ae, be[0], v16f{});
-      acc[i][1] = mma_fp8(ae, be[1], v16f{});
+      sp0 = scale_product(sa[i], sb[0]);
+      acc0 = mma_fp6(a0, b0[0], v16f{});
+      acc0 = mma_fp6(a1, b1[0], acc0);
+      if (i > 0) apply(i - 1, 1, acc1, sp1, s);
       __builtin_amdgcn_sched_barrier(0);
-      if (i > 0) apply(i - 1, 1, acc[i - 1][1], sp[i - 1][1], s);
-      sp[i][1] = scale_product(sa[i], sb[1]);
-      acc[i][0] = mma_fp8(ao, bo[0], acc[i][0]);
-      acc[i][1] = mma_fp8(ao, bo[1], acc[i][1]);
+      sp1 = scale_product(sa[i], sb[1]);
+      acc1 = mma_fp6(a0, b0[1], v16f{});
+      acc1 = mma_fp6(a1, b1[1], acc1);
+      apply(i, 0, acc0, sp0, s);
       __builtin_amdgcn_sched_barrier(0);
     }
-    apply(T::kTM - 1, 0, acc[T::kTM - 1][0], sp[T::kTM - 1][0], s);
-    apply(T::kTM - 1, 1, acc[T::kTM - 1][1], sp[T::kTM - 1][1], s);
+    apply(T::kTM - 1, 1, acc1, sp1, s);
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kPerStage));   // own copy of stage s+2 landed, reads done
     wg_barrier();
 #pragma unroll

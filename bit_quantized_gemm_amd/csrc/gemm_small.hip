@@ -12,17 +12,17 @@
 // kSmallMaxGroups INT4 groups (the last range also takes the INT8 outlier group); the
 // workgroup has one wave per range, at most 16, and a wave takes every 16th range when there
 // are more.  A wave issues every load of a range at once straight into registers (no LDS
-// staging, no barrier), then runs one 16 x 16 x 128 fp8 MFMA per group.  At the end the waves'
+// staging, no barrier), then runs one 16 x 16 x 128 fp6 MFMA per group.  At the end the waves'
 // fp32 sums meet in LDS and wave 0 adds them in wave order and writes Y: one kernel, no
 // scratch, deterministic.
 //
 // Operands.  Lane l supplies row (A: weight column n0 + l % 16; B: token row l % 16) and the
-// 32-byte K slice l / 16 of each operand.  Slices 0 and 1 take the even codes of packed bytes
-// 0-31 and 32-63 of the group's 64-byte stage (w & 0x87878787: fp8 e4m3 subnormals q * 2^-9),
-// slices 2 and 3 the odd codes of the same bytes (rotr(w, 4) & 0x87878787); both operands use
-// the same assignment, so every code of the group meets its partner once.  With the weights
-// as the first operand the 16 x 16 accumulator holds the output transposed: lane l owns token
-// row l % 16 and the four consecutive output columns 4 (l / 16) .. 4 (l / 16) + 3.
+// K slice l / 16 of each operand: the 32 codes in bytes 16 (l / 16) .. 16 (l / 16) + 15 of the
+// group's 64-byte stage, two packed units, which four bit operations per unit turn into six
+// words of fp6 e2m3 fields (the subnormal q / 8; the layout is described in atom_internal.h).
+// Both operands use the same assignment, so every code of the group meets its partner once.
+// With the weights as the first operand the 16 x 16 accumulator holds the output transposed:
+// lane l owns token row l % 16 and the four consecutive output columns 4 (l / 16) .. + 3.
 //
 // Scales.  v_mfma_f32_16x16x16_f16 with each lane's fp16 scale in element 0 of its four
 // K values gives 4 * sw * sx exactly (four equal exact products) in the accumulator layout;
@@ -42,16 +42,22 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCols = 16;                    // output columns per workgroup
-constexpr uint32_t kFp8Mask = 0x87878787u;   // sign bit and 3-bit magnitude of each byte
-constexpr int kScaleE8M0 = 127 + 9;          // 2^9: the e4m3 subnormal q * 2^-9 counts as q
+constexpr int kScaleE8M0 = 127 + 3;          // 2^3: the e2m3 subnormal q / 8 counts as q
 
-// 32 packed bytes (two 16-byte loads) -> 32 fp8 operand bytes: the even codes (rot = 0) or the
-// odd codes (rot = 4) of each 32-bit word.
-__device__ __forceinline__ v8i decode32(uint4 lo, uint4 hi, int rot) {
-  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+// Two packed units (16 bytes) -> the fp6 operand of their 32 codes (six words; the last two
+// are not read by the fp6 MFMA).
+__device__ __forceinline__ v8i fp6_operand(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   v8i r;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) r[k] = (int)(__builtin_amdgcn_alignbit(w[k], w[k], rot) & kFp8Mask);
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t w0 = w[2 * u], w1 = w[2 * u + 1];
+    r[3 * u] = (int)(w0 & ~kFp6Exp0);
+    r[3 * u + 1] = (int)(w1 & ~kFp6Exp1);
+    r[3 * u + 2] = (int)((w0 & kFp6Exp0) | (w1 & kFp6Exp1));
+  }
+  r[6] = 0;
+  r[7] = 0;
   return r;
 }
 
@@ -76,25 +82,22 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
   const int n0 = blockIdx.x * kCols;
   // rows past N / M repeat the last valid one; their results are never stored
   const int n = min(n0 + r, N - 1), m = min(r, M - 1);
-  const uint8_t* wrow = Wq + (size_t)n * rb + 32 * (slice & 1);
-  const uint8_t* xrow = Xq + (size_t)m * rb + 32 * (slice & 1);
-  const int rot = 4 * (slice >> 1);
+  const uint8_t* wrow = Wq + (size_t)n * rb + 16 * slice;
+  const uint8_t* xrow = Xq + (size_t)m * rb + 16 * slice;
 
   v4f yacc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int range = wave; range < ranges; range += waves) {
     const int ga = range * (G - 1) / ranges, gb = (range + 1) * (G - 1) / ranges;   // 1 .. kSmallMaxGroups
     const int ng = gb - ga;                                                         // uniform
     // every load of the range, issued before any of it is used
-    uint4 wl[kSmallMaxGroups][2], xl[kSmallMaxGroups][2];
+    uint4 wl[kSmallMaxGroups], xl[kSmallMaxGroups];
     uint16_t wsc[kSmallMaxGroups], xsc[kSmallMaxGroups];
 #pragma unroll
     for (int i = 0; i < kSmallMaxGroups; ++i) {
       if (i < ng) {
         const int g = ga + i;
-        wl[i][0] = *reinterpret_cast<const uint4*>(wrow + (size_t)g * 64);
-        wl[i][1] = *reinterpret_cast<const uint4*>(wrow + (size_t)g * 64 + 16);
-        xl[i][0] = *reinterpret_cast<const uint4*>(xrow + (size_t)g * 64);
-        xl[i][1] = *reinterpret_cast<const uint4*>(xrow + (size_t)g * 64 + 16);
+        wl[i] = *reinterpret_cast<const uint4*>(wrow + (size_t)g * 64);
+        xl[i] = *reinterpret_cast<const uint4*>(xrow + (size_t)g * 64);
         wsc[i] = sw[(size_t)g * N + n];
         xsc[i] = sx[(size_t)g * M + m];
       }
@@ -102,9 +105,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
 #pragma unroll
     for (int i = 0; i < kSmallMaxGroups; ++i) {
       if (i < ng) {
-        const v8i a = decode32(wl[i][0], wl[i][1], rot);
-        const v8i b = decode32(xl[i][0], xl[i][1], rot);
-        const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{}, 0, 0, 0, kScaleE8M0, 0, kScaleE8M0);
+        const v8i a = fp6_operand(wl[i]);
+        const v8i b = fp6_operand(xl[i]);
+        // cbsz = blgp = 2: both operands fp6 e2m3
+        const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{}, 2, 2, 0, kScaleE8M0, 0, kScaleE8M0);
         const v4f sp = __builtin_amdgcn_mfma_f32_16x16x16f16(scale_operand(wsc[i]), scale_operand(xsc[i]), v4f{}, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) yacc[j] = __builtin_fmaf(acc[j], sp[j], yacc[j]);

@@ -1,5 +1,5 @@
 // Row quantize for gfx950: reorder through perm, per-128 group absmax, fp16 scale,
-// INT4 codes packed two per byte, INT8 codes for the 128-channel outlier tail.
+// INT4 codes packed four bits each, INT8 codes for the 128-channel outlier tail.
 //
 // One kernel serves both the runtime activation quantize (rows = tokens) and the offline
 // weight pack (rows = output channels): the quantization record "Atom (mixed-precision
@@ -28,10 +28,12 @@
 // Adding 1.5*2^23 rounds the clamped value (or its magnitude) to that integer with ties to
 // even and leaves its two's-complement low byte in the low bits of the sum.
 //
-// Packed INT4 layout (sign-magnitude, chosen so that a GEMM can turn a word into fp8 e4m3
-// subnormals with one AND per parity): per 32-bit word of codes c0..c7, byte j holds |c_2j|
-// in bits 0-2, |c_2j+1| in bits 4-6, the sign of c_2j in bit 7 and the sign of c_2j-1 (byte
-// 0: of c7) in bit 3.
+// Packed INT4 layout (chosen so that a GEMM turns 16 codes into fp6 e2m3 MFMA operands with
+// four bit operations): a unit of 16 consecutive codes c0..c15 is 8 bytes.  Code c_i is the
+// fp6 e2m3 field f_i = |c_i| | (c_i < 0) << 5 (the subnormal c_i / 8) at bits 6i .. 6i+5 of a
+// 96-bit string T0:T1:T2; the exponent bits (3 and 4 of every field) are zero, and T2's bits
+// lie exactly at the exponent positions of T0 (kFp6Exp0) and T1 (kFp6Exp1), so the unit is
+// stored as the words T0 | (T2 & kFp6Exp0), T1 | (T2 & kFp6Exp1).
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
@@ -164,24 +166,19 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) b[i] = __float_as_uint(v[i] + kRound);
     if (!tail) {
-      // sign-magnitude INT4: per 32-bit word of codes c0..c7, byte j = |c_2j| | |c_2j+1| << 4 |
-      // sign(c_2j) << 7 | sign(c_2j-1) << 3 (byte 0 takes the sign of c7)
-      uint32_t m[kPerThread];                            // |code| in the low byte
+      // INT4 unit: fp6 fields f_i at bits 6i of T0:T1:T2, T2 folded into the exponent bits
+      uint32_t f[kPerThread];
 #pragma unroll
-      for (int i = 0; i < kPerThread; ++i) m[i] = __float_as_uint(__builtin_fabsf(v[i]) + kRound);
-      uint2 w;
-      uint32_t word[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int o = 8 * h;
-        const uint32_t ev = ((pack4(b[o], b[o + 2], b[o + 4], b[o + 6]) & 0x80808080u) |
-                             pack4(m[o], m[o + 2], m[o + 4], m[o + 6]));
-        const uint32_t od = (pack4(b[o + 1], b[o + 3], b[o + 5], b[o + 7]) & 0x80808080u) |
-                            pack4(m[o + 1], m[o + 3], m[o + 5], m[o + 7]);
-        word[h] = ev | ((od << 4) | (od >> 28));         // odd magnitudes to bits 4-6, odd signs to the next byte
+      for (int i = 0; i < kPerThread; ++i) {
+        const uint32_t m = __float_as_uint(__builtin_fabsf(v[i]) + kRound) & 7u;   // |code|
+        f[i] = (b[i] & 0x20u) | m;   // bits 3-7 of a two's-complement code in [-7, 7] equal its sign
       }
-      w.x = word[0];
-      w.y = word[1];
+      const uint32_t t0 = f[0] | f[1] << 6 | f[2] << 12 | f[3] << 18 | f[4] << 24 | f[5] << 30;
+      const uint32_t t1 = f[5] >> 2 | f[6] << 4 | f[7] << 10 | f[8] << 16 | f[9] << 22 | f[10] << 28;
+      const uint32_t t2 = f[10] >> 4 | f[11] << 2 | f[12] << 8 | f[13] << 14 | f[14] << 20 | f[15] << 26;
+      uint2 w;
+      w.x = t0 | (t2 & kFp6Exp0);
+      w.y = t1 | (t2 & kFp6Exp1);
       *reinterpret_cast<uint2*>(qrow + c / 2) = w;
     } else {
       u32x4 w;

@@ -21,11 +21,14 @@
  *     <= ATOM_MAX_ROWS.  G = K/128 groups: groups 0..G-2 are INT4, group G-1 is the INT8
  *     outlier group.  RB = atom_row_bytes(K) = (K-128)/2 + 128 bytes per packed row.
  *   - Packed row format: the first (K-128)/2 bytes hold the K-128 reordered INT4 codes in
- *     [-7, 7], sign-magnitude, in 32-bit little-endian words of eight consecutive codes
- *     c0..c7.  Byte j (0..3) of a word holds |c_2j| in bits 0-2, the sign of c_2j in bit 7,
- *     |c_2j+1| in bits 4-6, and in bit 3 the sign of c_2j-1 (byte 0: the sign of c7); a sign
- *     bit is 1 exactly when its code is negative.  (w & 0x87878787 then gives the even codes
- *     and rotr(w, 4) & 0x87878787 the odd codes as fp8 e4m3 values q * 2^-9.)  The last 128
+ *     [-7, 7], four bits per code, in units of 16 consecutive codes c0..c15 stored as two
+ *     32-bit little-endian words w0, w1.  Code c_i is the 6-bit field
+ *     f_i = |c_i| + 32 * (c_i < 0) (the fp6 e2m3 encoding of c_i / 8, a subnormal) at bits
+ *     6i .. 6i+5 of a 96-bit string T0 + T1 * 2^32 + T2 * 2^64, and
+ *     w0 = T0 | (T2 & 0x18618618), w1 = T1 | (T2 & 0x86186186): the masks are the exponent
+ *     bits (3 and 4 of each field) of T0 and T1, which are always zero, and T2's other bits
+ *     are zero too.  (Decoding back to fp6 MFMA operands: T0 = w0 & ~0x18618618,
+ *     T1 = w1 & ~0x86186186, T2 = (w0 & 0x18618618) | (w1 & 0x86186186).)  The last 128
  *     bytes hold the INT8 outlier codes in [-127, 127], two's complement.  Scales are fp16,
  *     group-major [G, rows].
  *   - Argument checks run on the host before any HIP call and return the status without

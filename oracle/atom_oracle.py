@@ -30,9 +30,11 @@ Readings taken where the pages are silent (each one is also a parameter of the H
 * scale: fp32 correctly rounded ``absmax / qmax``, rounded to nearest-even fp16 and stored
   fp16, group-major ``[G, rows]``; codes ``clamp(rint_even(fl32(x / s)))``; a zero scale
   gives zero codes;
-* packing: INT4 codes in sign-magnitude form, two per byte, with each odd code's sign bit
-  rotated into the next byte of its 32-bit word (see ``pack_rows``); the 128 INT8 outlier
-  codes are appended as the last 128 two's-complement bytes of each row;
+* packing: INT4 codes four bits each, in units of 16 consecutive codes stored in 8 bytes:
+  the codes' OCP FP6 E2M3 encodings (value code/8, a subnormal) laid end to end make 96
+  bits, and the last 32 of them are folded into the first 64 at the exponent bits, which
+  are always zero for these codes (see ``pack_rows``); the 128 INT8 outlier codes are
+  appended as the last 128 two's-complement bytes of each row;
 * output: ``Y = sum_g acc_g * sx_g * sw_g`` rounded once to fp16 (round to nearest even).
 """
 from __future__ import annotations
@@ -128,25 +130,47 @@ def quantize_rows(X: np.ndarray, perm: np.ndarray):
 
 
 # --------------------------------------------------------------------------- step: pack / unpack
+# INT4 packing unit: 16 codes -> 8 bytes.  Code c is written as the 6-bit FP6 E2M3 field of
+# the value c/8: sign in bit 5, exponent bits 3-4 (zero: c/8 is a subnormal), |c| in bits 0-2.
+UNIT = 16
+FIELD = 6
+_EXP_BITS = (3, 4)   # exponent positions inside a field
+
+
+def _exponent_mask(word: int) -> int:
+    """Bits of 32-bit word ``word`` (0, 1, 2) of the 96-bit field string that are exponent
+    bits of some field, i.e. always zero for INT4 codes."""
+    return sum(1 << b for b in range(32) if (32 * word + b) % FIELD in _EXP_BITS)
+
+
+E0, E1, E2 = (_exponent_mask(w) for w in range(3))
+# The third word's nonzero bits are exactly the exponent positions of the first two words,
+# so it can be stored in them (a fact of the 6-bit period: 32 = 2 mod 6, 64 = 4 mod 6).
+assert (0xFFFFFFFF & ~E2) == (E0 | E1) and (E0 & E1) == 0
+
+
 def pack_rows(codes: np.ndarray) -> np.ndarray:
     """int8 codes [rows, K] -> packed bytes [rows, (K-128)/2 + 128].
 
-    INT4 codes (the first K-128 reordered channels) are stored in sign-magnitude form, two
-    per byte, in 32-bit words of eight consecutive codes c0..c7.  Byte j of a word holds
-    |c_{2j}| in bits 0-2, the sign of c_{2j} in bit 7, |c_{2j+1}| in bits 4-6, and in bit 3 the
-    sign of the odd code c_{2j-1} of the previous byte (byte 0 holds the sign of c7).  The
-    sign bit is 1 exactly when the code is negative.  The 128 INT8 outlier codes follow as
+    The first K-128 (INT4) codes go in units of 16 consecutive codes c0..c15, 8 bytes per
+    unit, units in order.  Code c_i becomes the field f_i = |c_i| + 32 * (c_i < 0) at bits
+    6i .. 6i+5 of a 96-bit string T = T0 + T1 * 2^32 + T2 * 2^64.  The stored words are
+    w0 = T0 | (T2 & E0) and w1 = T1 | (T2 & E1), where E0 / E1 are the exponent-bit
+    positions of T0 / T1 (zero there, since |c_i| <= 7 keeps every field a subnormal).
+    w0 and w1 are written little-endian.  The 128 INT8 outlier codes follow as
     two's-complement bytes."""
     codes = np.asarray(codes, dtype=np.int8)
     rows, K = codes.shape
     klo = K - OUTLIERS
-    q = codes[:, :klo].astype(np.int16).reshape(rows, klo // 8, 4, 2)     # [row, word, byte j, even/odd]
-    mag = np.abs(q).astype(np.uint8)
-    neg = (q < 0).astype(np.uint8)
-    even_m, odd_m = mag[..., 0], mag[..., 1]
-    even_s, odd_s = neg[..., 0], neg[..., 1]
-    odd_s_prev = np.roll(odd_s, 1, axis=2)                                 # byte j <- sign of byte j-1's odd code
-    body = (even_m | (odd_m << 4) | (even_s << 7) | (odd_s_prev << 3)).astype(np.uint8).reshape(rows, klo // 2)
+    q = codes[:, :klo].astype(np.int64).reshape(rows, klo // UNIT, UNIT)
+    f = np.abs(q) + 32 * (q < 0)                                            # [row, unit, i]
+    bits = (f[..., None] >> np.arange(FIELD)) & 1                          # [row, unit, i, b]
+    bits = bits.reshape(rows, klo // UNIT, 3, 32)                          # bit 6i+b of T, by word
+    T = (bits << np.arange(32, dtype=np.int64)).sum(axis=-1)               # [row, unit, word]
+    w0 = T[..., 0] | (T[..., 2] & E0)
+    w1 = T[..., 1] | (T[..., 2] & E1)
+    words = np.stack([w0, w1], axis=-1).astype("<u4")                      # [row, unit, 2]
+    body = words.view(np.uint8).reshape(rows, klo // 2)
     tail = codes[:, klo:].view(np.uint8)
     return np.ascontiguousarray(np.concatenate([body, tail], axis=1))
 
@@ -158,14 +182,16 @@ def unpack_rows(packed: np.ndarray, K: int) -> np.ndarray:
     if packed.shape[1] != row_bytes(K):
         raise ValueError("packed row length does not match K")
     klo = K - OUTLIERS
-    b = packed[:, : klo // 2].astype(np.int16).reshape(rows, klo // 8, 4)
-    even_m, odd_m = b & 7, (b >> 4) & 7
-    even_s = (b >> 7) & 1
-    odd_s = np.roll((b >> 3) & 1, -1, axis=2)                              # byte j's odd sign sits in byte j+1
-    even = np.where(even_s == 1, -even_m, even_m)
-    odd = np.where(odd_s == 1, -odd_m, odd_m)
+    words = np.ascontiguousarray(packed[:, : klo // 2]).view("<u4").astype(np.int64).reshape(rows, klo // UNIT, 2)
+    w0, w1 = words[..., 0], words[..., 1]
+    T = np.stack([w0 & ~E0 & 0xFFFFFFFF, w1 & ~E1 & 0xFFFFFFFF, (w0 & E0) | (w1 & E1)], axis=-1)
+    bits = (T[..., None] >> np.arange(32)) & 1                              # [row, unit, word, b]
+    f = (bits.reshape(rows, klo // UNIT, UNIT, FIELD) << np.arange(FIELD)).sum(axis=-1)
+    if np.any(f & 0b011000):
+        raise ValueError("exponent bits set: not an INT4 code")
+    mag, neg = f & 7, f >> 5
     out = np.empty((rows, K), dtype=np.int8)
-    out[:, :klo] = np.stack([even, odd], axis=-1).reshape(rows, klo)
+    out[:, :klo] = np.where(neg == 1, -mag, mag).reshape(rows, klo)
     out[:, klo:] = packed[:, klo // 2:].view(np.int8)
     return out
 

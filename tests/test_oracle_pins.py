@@ -24,8 +24,9 @@ def _h(hexstr):
 
 # --------------------------------------------------------------------------- hand-worked rows
 def test_worked_rows_fixture():
-    """Codes, scales and bytes of four hand-derived rows (ties, outlier group, zero row,
-    underflowing scale, subnormal scale where the clamp fires)."""
+    """Codes, scales and bytes of five hand-derived rows (ties, outlier group, zero row,
+    underflowing scale, subnormal scale where the clamp fires, and a unit whose 16 codes
+    fill every FP6 field, including the folded third word)."""
     fx = json.load(open(os.path.join(GOLDEN, "worked_rows.json")))
     K = fx["K"]
     rows = fx["rows"]
