@@ -158,6 +158,30 @@ def test_group_acc_bitexact(key):
     np.testing.assert_array_equal(acc, O.group_acc(qx, qw))
 
 
+@pytest.mark.parametrize("M,N", [(15, 40), (45, 150)])
+def test_oracle_packed_units_every_code_in_every_field(M, N):
+    """The GEMMs read packed rows written by the oracle's packer (not by the GPU quantize):
+    every INT4 code value sits in every field position of a 16-code unit, the folded third
+    word included, and the INT8 group spans [-127, 127].  Group accumulators bit-exact; Y
+    within tolerance on the few-rows kernel (M <= 16) and the tiled kernel."""
+    K = 1152
+    klo, G = K - O.OUTLIERS, K // O.GROUP
+    _say(f"[units] M={M} N={N} K={K}")
+    m, n, k = np.arange(M)[:, None], np.arange(N)[:, None], np.arange(K)[None, :]
+    qx = ((m + k) % 15 - 7).astype(np.int8)                     # rows cycle through all 15 codes
+    qw = ((n + 7 * k + k // 16) % 15 - 7).astype(np.int8)
+    qx[:, klo:] = ((37 * m + 11 * k[:, klo:]) % 255 - 127).astype(np.int8)
+    qw[:, klo:] = ((53 * n + 5 * k[:, klo:]) % 255 - 127).astype(np.int8)
+    for i in range(16):                                          # coverage of the test itself
+        assert len(np.unique(qx[:, :klo][:, i::16])) == 15 and len(np.unique(qw[:, :klo][:, i::16])) == 15
+    Xq, Wq = dev(O.pack_rows(qx)), dev(O.pack_rows(qw))
+    np.testing.assert_array_equal(host(bq.atom_gemm_group_acc(Xq, Wq, K)), O.group_acc(qx, qw))
+    sx = (2.0 ** -(6 + (np.arange(G)[:, None] + m.T) % 5) * (1 + (m.T % 3) / 4)).astype(np.float16)
+    sw = (2.0 ** -(4 + (2 * np.arange(G)[:, None] + n.T) % 7) * (1 + (n.T % 5) / 8)).astype(np.float16)
+    Y = host(bq.atom_gemm(Xq, dev(sx), Wq, dev(sw), K))
+    assert_y_close(Y, O.gemm_ref(qx, sx, qw, sw), f"units {M}x{N}")
+
+
 # --------------------------------------------------------------------------- a5: output
 @pytest.mark.parametrize("key", ["T", "A"])
 def test_gemm_full_output(key):
