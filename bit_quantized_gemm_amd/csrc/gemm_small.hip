@@ -89,43 +89,51 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
   for (int range = wave; range < ranges; range += waves) {
     const int ga = range * (G - 1) / ranges, gb = (range + 1) * (G - 1) / ranges;   // 1 .. kSmallMaxGroups
     const int ng = gb - ga;                                                         // uniform
-    // every load of the range, issued before any of it is used
+    const bool last = range == ranges - 1;                                          // uniform
+    // Every load of the range is issued, unconditionally, before any of it is used (a load
+    // under a branch would first wait for all earlier ones).  Groups past the range's end
+    // repeat its last group, and outside the last range the INT8 group's loads repeat group
+    // ga's bytes and scales: in bounds, cached, never used.
     uint4 wl[kSmallMaxGroups], xl[kSmallMaxGroups];
     uint16_t wsc[kSmallMaxGroups], xsc[kSmallMaxGroups];
 #pragma unroll
     for (int i = 0; i < kSmallMaxGroups; ++i) {
-      if (i < ng) {
-        const int g = ga + i;
-        wl[i] = *reinterpret_cast<const uint4*>(wrow + (size_t)g * 64);
-        xl[i] = *reinterpret_cast<const uint4*>(xrow + (size_t)g * 64);
-        wsc[i] = sw[(size_t)g * N + n];
-        xsc[i] = sx[(size_t)g * M + m];
-      }
+      const int g = min(ga + i, gb - 1);
+      wl[i] = *reinterpret_cast<const uint4*>(wrow + (size_t)g * 64);
+      xl[i] = *reinterpret_cast<const uint4*>(xrow + (size_t)g * 64);
+      wsc[i] = sw[(size_t)g * N + n];
+      xsc[i] = sx[(size_t)g * M + m];
     }
+    // INT8 outlier group: the 16-byte K slice of each 64-byte half
+    const size_t o8 = last ? rb - ATOM_OUTLIERS : (size_t)ga * 64;
+    const size_t c8 = last ? 64 : 0;
+    const int g8 = last ? G - 1 : ga;
+    v4i w8[2], x8[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      w8[c] = *reinterpret_cast<const v4i*>(Wq + (size_t)n * rb + o8 + 16 * slice + c8 * c);
+      x8[c] = *reinterpret_cast<const v4i*>(Xq + (size_t)m * rb + o8 + 16 * slice + c8 * c);
+    }
+    const uint16_t wsc8 = sw[(size_t)g8 * N + n], xsc8 = sx[(size_t)g8 * M + m];
+    __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the first use
+    // Branch-free as well (a load used only under a branch gets sunk into it): a repeated
+    // group gets a zero scale product and adds exactly +0.
 #pragma unroll
     for (int i = 0; i < kSmallMaxGroups; ++i) {
-      if (i < ng) {
-        const v8i a = fp6_operand(wl[i]);
-        const v8i b = fp6_operand(xl[i]);
-        // cbsz = blgp = 2: both operands fp6 e2m3
-        const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{}, 2, 2, 0, kScaleE8M0, 0, kScaleE8M0);
-        const v4f sp = __builtin_amdgcn_mfma_f32_16x16x16f16(scale_operand(wsc[i]), scale_operand(xsc[i]), v4f{}, 0, 0, 0);
+      const v8i a = fp6_operand(wl[i]);
+      const v8i b = fp6_operand(xl[i]);
+      // cbsz = blgp = 2: both operands fp6 e2m3
+      const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{}, 2, 2, 0, kScaleE8M0, 0, kScaleE8M0);
+      const uint16_t ws = i < ng ? wsc[i] : (uint16_t)0;
+      const v4f sp = __builtin_amdgcn_mfma_f32_16x16x16f16(scale_operand(ws), scale_operand(xsc[i]), v4f{}, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) yacc[j] = __builtin_fmaf(acc[j], sp[j], yacc[j]);
-      }
+      for (int j = 0; j < 4; ++j) yacc[j] = __builtin_fmaf(acc[j], sp[j], yacc[j]);
     }
-    if (range == ranges - 1) {   // INT8 outlier group: 16-byte K slice of each 64-byte half
-      const size_t o = rb - ATOM_OUTLIERS + 16 * slice;
-      v4i w8[2], x8[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        w8[c] = *reinterpret_cast<const v4i*>(Wq + (size_t)n * rb + o + 64 * c);
-        x8[c] = *reinterpret_cast<const v4i*>(Xq + (size_t)m * rb + o + 64 * c);
-      }
-      const uint16_t wsc8 = sw[(size_t)(G - 1) * N + n], xsc8 = sx[(size_t)(G - 1) * M + m];
+    {   // INT8 group, counted by the last range only (zero scale product elsewhere)
       v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8[0], x8[0], v4i{}, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8[1], x8[1], acc, 0, 0, 0);
-      const v4f sp = __builtin_amdgcn_mfma_f32_16x16x16f16(scale_operand(wsc8), scale_operand(xsc8), v4f{}, 0, 0, 0);
+      const uint16_t ws = last ? wsc8 : (uint16_t)0;
+      const v4f sp = __builtin_amdgcn_mfma_f32_16x16x16f16(scale_operand(ws), scale_operand(xsc8), v4f{}, 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) yacc[j] = __builtin_fmaf((float)acc[j], sp[j], yacc[j]);   // |acc| < 2^24: exact
     }
