@@ -119,7 +119,7 @@ int atom_quantize_act(const void* X, const int32_t* perm, int32_t M, int32_t K, 
 
 int64_t atom_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
   if (!valid_gemm(M, N, K)) return -(int64_t)ATOM_E_SHAPE;
-  return atom::gemm_workspace_bytes(atom::gemm_plan(M, N, K), M, N);
+  return atom::gemm_workspace_bytes(atom::gemm_plan(M, N, K));
 }
 
 int atom_gemm_ws(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N, int32_t K,
@@ -128,7 +128,7 @@ int atom_gemm_ws(const void* Xq, const void* sx, const void* Wq, const void* sw,
   if (!valid_gemm(M, N, K)) return ATOM_E_SHAPE;
   if (!aligned16(Xq) || !aligned16(sx) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y)) return ATOM_E_ALIGN;
   atom::GemmPlan plan = atom::gemm_plan(M, N, K);
-  int64_t need = atom::gemm_workspace_bytes(plan, M, N);
+  int64_t need = atom::gemm_workspace_bytes(plan);
   if (need > 0 && (!workspace || workspace_bytes < need)) {   // too little scratch: the 128 x 128 kernel, unsplit
     plan = atom::GemmPlan{((M + 127) / 128) * ((N + 127) / 128), 0, 1, 0};
     need = 0;

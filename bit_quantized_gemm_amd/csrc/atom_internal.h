@@ -34,8 +34,8 @@ struct GemmPlan {
 constexpr int kSmallMaxM = 16, kSmallMaxGroups = 4;
 GemmPlan gemm_plan(int M, int N, int K);
 // Scratch bytes the plan needs (0 when it writes Y directly).
-int64_t gemm_workspace_bytes(const GemmPlan& plan, int M, int N);
-// `part` holds gemm_workspace_bytes(plan, M, N) bytes of scratch when that is > 0, else unused.
+int64_t gemm_workspace_bytes(const GemmPlan& plan);
+// `part` holds gemm_workspace_bytes(plan) bytes of scratch when that is > 0, else unused.
 hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
                        int K, uint16_t* Y, float* part, const GemmPlan& plan, hipStream_t stream);
 // Few-rows kernel (M <= kSmallMaxM), Y written directly.

@@ -575,7 +575,7 @@ GemmPlan gemm_plan(int M, int N, int K) {
   return s < 2 ? GemmPlan{tiles, 0, 1, 0} : GemmPlan{0, tiles, s, 0};
 }
 
-int64_t gemm_workspace_bytes(const GemmPlan& plan, int M, int N) {
+int64_t gemm_workspace_bytes(const GemmPlan& plan) {
   if (plan.small) return 0;
   return plan.rem > 0 ? (int64_t)plan.rem * plan.splits * kBM * kBN * (int64_t)sizeof(float) : 0;
 }
