@@ -280,7 +280,8 @@ def main():
         q = [evl[i][si][0].elapsed_time(evl[i][si][1]) for i in range(n_k)]
         g = [evl[i][si][1].elapsed_time(evl[i][si][2]) for i in range(n_k)]
         per[s["key"]] = dict(quant_us=1e3 * float(np.mean(q)), gemm_us=1e3 * float(np.mean(g)),
-                             quant_us_median=1e3 * float(np.median(q)), gemm_us_median=1e3 * float(np.median(g)))
+                             quant_us_p10_50_90=[round(1e3 * float(v), 2) for v in np.percentile(q, [10, 50, 90])],
+                             gemm_us_p10_50_90=[round(1e3 * float(v), 2) for v in np.percentile(g, [10, 50, 90])])
 
     ops_step = sum(s["w"].ops for s in sets)
     value = ops_step / (ms_per_step * 1e-3) / 1e12
@@ -298,6 +299,7 @@ def main():
         shapes[w.key] = {
             "name": w.name, "M": w.M, "K": w.K, "N": w.N,
             "quant_us": round(p["quant_us"], 2), "gemm_us": round(p["gemm_us"], 2),
+            "quant_us_p10_50_90": p["quant_us_p10_50_90"], "gemm_us_p10_50_90": p["gemm_us_p10_50_90"],
             "gemm_tops": round(w.ops / (p["gemm_us"] * 1e-6) / 1e12, 1),
             "gemm_frac_int8_peak": round(w.ops / (p["gemm_us"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4),
             "gemm_frac_fp6_peak": round(w.ops / (p["gemm_us"] * 1e-6) / 1e12 / FP6_PEAK_TOPS, 4),

@@ -183,29 +183,16 @@ def test_oracle_packed_units_every_code_in_every_field(M, N):
 
 
 # --------------------------------------------------------------------------- a5: output
-@pytest.mark.parametrize("key", ["T", "A"])
+@pytest.mark.parametrize("key", ["T", "A", "B", "C"])
 def test_gemm_full_output(key):
+    """Every element of Y for the tiny workload and the three Llama-7B shapes (the oracle's
+    fp64 dequantise-then-matmul takes a few seconds at 2048 x 4096 x 11008)."""
     w, x, wt, perm = workload(key)
     _say(f"[Y] {key} full")
     Wq, sw = bq.atom_pack_weights(dev(wt), dev(perm))
     Y = host(bq.linear(dev(x), dev(perm), Wq, sw))
     _, y64, _, _ = O.linear(x, wt, perm)
     assert_y_close(Y, y64, key)
-
-
-@pytest.mark.parametrize("key", ["B", "C"])
-def test_gemm_sampled_output(key):
-    w, x, wt, perm = workload(key)
-    _say(f"[Y] {key} sampled")
-    Wq, sw = bq.atom_pack_weights(dev(wt), dev(perm))
-    Y = host(bq.linear(dev(x), dev(perm), Wq, sw))
-    rng = np.random.default_rng(123)
-    rows = np.sort(rng.choice(w.M, 256, replace=False))
-    cols = np.sort(rng.choice(w.N, 1024, replace=False))
-    qx, sx = O.quantize_rows(x[rows], perm)
-    qw, sw_ref = O.quantize_rows(wt[cols], perm)
-    y64 = O.gemm_ref(qx, sx, qw, sw_ref)
-    assert_y_close(Y[np.ix_(rows, cols)], y64, key)
 
 
 def test_gemm_llama70b_sampled():
