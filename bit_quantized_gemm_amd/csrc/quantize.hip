@@ -51,8 +51,6 @@ constexpr int kThreads = 256;
 constexpr int kPerThread = 16;                       // reordered elements per thread per pass
 constexpr int kLanesPerGroup = ATOM_GROUP / kPerThread;   // 8
 
-__device__ __forceinline__ float half_bits_to_float(uint16_t h) { return __half2float(__ushort_as_half(h)); }
-
 // Column stride (32-bit words) of the staged row: the smallest value >= K/16 that is 8 mod 64.
 __host__ __device__ constexpr int staged_stride(int K) { return K / 16 + ((8 - K / 16) & 63); }
 
@@ -70,8 +68,12 @@ __device__ __forceinline__ float group_max8(float a) {
 
 // Clamped quotient of x for scale s (> 0) with reciprocal r; its nearest integer (ties to
 // even) is the code.
-__device__ __forceinline__ float code_value(float x, float s, float r, float qmax) {
-  const float t = x * r;
+__device__ __forceinline__ float code_value(_Float16 xh, float s, float r, float qmax) {
+  const float x = (float)xh;
+  // t = x * r, written as an fma with +0 so that it cannot become a plain multiply of a
+  // converted x: the two differ only in the sign of a zero product, which then rounds to the
+  // same code 0
+  const float t = __builtin_fmaf(x, r, 0.0f);
   const float e = __builtin_fmaf(-t, s, x);
   const float u = __builtin_fmaf(e, r, t);
   return __builtin_amdgcn_fmed3f(u, -qmax, qmax);
@@ -144,14 +146,16 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
   auto quantize16 = [&](int c, const int (&off)[kPerThread], uint8_t* qrow, int row) {
     const int g = c / ATOM_GROUP;
     const bool tail = g == G - 1;
-    float x[kPerThread];
-    float a = 0.0f;
+    // The elements stay fp16: the absmax is taken in fp16 (exact), and each fp32 step that
+    // reads x takes it as a mixed-precision fma operand, so no element is converted.
+    _Float16 x[kPerThread];
+    _Float16 ah = (_Float16)0.0f;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      x[i] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(lds_bytes + off[i]));
-      a = __builtin_fmaxf(a, __builtin_fabsf(x[i]));
+      x[i] = __builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(lds_bytes + off[i]));
+      ah = __builtin_fmaxf16(ah, __builtin_fabsf16(x[i]));
     }
-    a = group_max8(a);
+    const float a = group_max8((float)ah);
 
     const float qmax = tail ? 127.0f : 7.0f;
     const __half s16 = __float2half_rn(a / qmax);      // correctly rounded fp32 divide, then RNE to fp16
