@@ -7,7 +7,8 @@
 // (Field "Bits": w4a4; "Weight group size": 128; "notes": each contiguous 128-element group is
 // quantized independently, plus one 128-channel high-precision group).
 //
-// Work layout.  Persistent workgroups of 256 threads walk the rows.  A row is staged in LDS
+// Work layout.  Persistent workgroups of 256 threads walk the rows (for jobs of 2048 rows or
+// more, each XCD owns whole 64-row blocks, whose fp16 scales share cache lines).  A row is staged in LDS
 // (fp16, 16-byte loads); the next row's loads are issued into registers before the current
 // row is processed, so HBM reads overlap the arithmetic.  The staged row is stored by
 // columns: original element e = 16q + r sits in 32-bit word (r / 2) * QP + q, half r % 2,
@@ -50,6 +51,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kPerThread = 16;                       // reordered elements per thread per pass
 constexpr int kLanesPerGroup = ATOM_GROUP / kPerThread;   // 8
+constexpr int kXcdCount = 8;                         // accelerator complex dies, each with its own L2
+constexpr int kRowBlock = 64;                        // rows whose fp16 scales fill one 128-byte line
+constexpr int kBlockedMinRows = 2048;                // jobs of at least this many rows use XCD row blocks
 
 // Column stride (32-bit words) of the staged row: the smallest value >= K/16 that is 8 mod 64.
 __host__ __device__ constexpr int staged_stride(int K) { return K / 16 + ((8 - K / 16) & 63); }
@@ -195,11 +199,31 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
     if ((threadIdx.x & (kLanesPerGroup - 1)) == 0) S[(size_t)g * rows + row] = __half_as_ushort(s16);
   };
 
+  // Work items of this workgroup, k = 0, 1, ...  Large jobs (one item per row) give each XCD
+  // whole 64-row blocks (block b to XCD b % 8, workgroups reach the XCDs round-robin), so the
+  // 2-byte scale stores of a block's rows, which share cache lines of the group-major scale
+  // array, meet in one L2; the XCD's workgroups interleave over its rows.
+  const bool blocked = split == 1 && rows >= kBlockedMinRows && gridDim.x >= kXcdCount;   // uniform
+  const int xcd = blockIdx.x % kXcdCount, wx = blockIdx.x / kXcdCount;
+  const int nx = ((int)gridDim.x - xcd + kXcdCount - 1) / kXcdCount;      // workgroups on this XCD
+  const int nblk = (rows + kRowBlock - 1) / kRowBlock;
+  const int myblk = (nblk - xcd + kXcdCount - 1) / kXcdCount;               // blocks xcd, xcd + 8, ...
+  const int rx = myblk * kRowBlock - ((nblk - 1) % kXcdCount == xcd ? nblk * kRowBlock - rows : 0);
   const int items = rows * split;
-  int item = blockIdx.x;
-  if (item < items) prefetch(item / split);
-  for (; item < items; item += gridDim.x) {
-    const int row = item / split, part = item - row * split;
+  auto valid = [&](int k) {
+    return blocked ? wx + k * nx < rx : (int)blockIdx.x + k * (int)gridDim.x < items;
+  };
+  auto row_of = [&](int k) {
+    if (blocked) {
+      const int t = wx + k * nx;
+      return kRowBlock * (xcd + kXcdCount * (t / kRowBlock)) + t % kRowBlock;
+    }
+    return ((int)blockIdx.x + k * (int)gridDim.x) / split;
+  };
+  if (valid(0)) prefetch(row_of(0));
+  for (int k = 0; valid(k); ++k) {
+    const int row = row_of(k);
+    const int part = blocked ? 0 : ((int)blockIdx.x + k * (int)gridDim.x) - row * split;
     __syncthreads();                                 // everyone finished reading the previous row
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
@@ -214,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
       }
     }
     __syncthreads();
-    if (item + (int)gridDim.x < items) prefetch((item + gridDim.x) / split);   // next item's loads fly meanwhile
+    if (valid(k + 1)) prefetch(row_of(k + 1));       // next item's loads fly meanwhile
 
     uint8_t* qrow = Q + (size_t)row * rb;
     if (PASSES > 0) {
