@@ -8,9 +8,9 @@
 // quantized independently, plus one 128-channel high-precision group).
 //
 // Work layout.  Persistent workgroups of 256 threads walk the rows (for jobs of 2048 rows or
-// more, each XCD owns whole 64-row blocks, whose fp16 scales share cache lines).  A row is staged in LDS
-// (fp16, 16-byte loads); the next row's loads are issued into registers before the current
-// row is processed, so HBM reads overlap the arithmetic.  The staged row is stored by
+// more, each XCD owns whole 64-row blocks, whose fp16 scales share cache lines).  A row is
+// staged in LDS (fp16, 16-byte loads); the next row's loads are issued into registers before
+// the current row is processed, so HBM reads overlap the arithmetic.  The staged row is stored by
 // columns: original element e = 16q + r sits in 32-bit word (r / 2) * QP + q, half r % 2,
 // where QP >= K/16 is padded to 8 mod 64.  A thread reads 16 consecutive reordered elements,
 // which for neighbouring lanes lie 16 elements apart in the row, so the lanes of one read hit
