@@ -535,22 +535,28 @@ constexpr int kSplitMinTiles = 128, kSplitTargetBlocks = 256, kSplitMinGroups = 
 
 // Y of the split tiles = fp16(0.5 * sum over pieces of the partial tiles), pieces added in
 // order.  blockIdx.y = split tile (tile full + blockIdx.y in tile order); four consecutive
-// outputs of one tile row per thread.
+// outputs of one tile row per thread.  The piece count S is a template argument so that all S
+// loads are in flight before the first add: with a run-time count the loop waits for each load
+// in turn (64 x 4096 x 4096, seven pieces: the GEMM call takes 14.5 us instead of 19.6 us).
+template <int S>
 __global__ __launch_bounds__(256) void gemm_splitk_finish_kernel(const float* __restrict__ part, int full, int rem,
-                                                                 int splits, int M, int N, uint16_t* __restrict__ Y) {
+                                                                 int M, int N, uint16_t* __restrict__ Y) {
   const int t = blockIdx.y;
   const int e = (blockIdx.x * 256 + threadIdx.x) * 4;       // element of the tile, < kBM * kBN
   const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
   const int2 tc = tile_coords(full + t, tiles_m, tiles_n);
   const int m = tc.x * kBM + e / kBN, n = tc.y * kBN + e % kBN;
   const float* src = part + (size_t)t * (kBM * kBN) + e;
-  float4 acc = *reinterpret_cast<const float4*>(src);
-  for (int k = 1; k < splits; ++k) {
-    const float4 v = *reinterpret_cast<const float4*>(src + (size_t)k * rem * (kBM * kBN));
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+  float4 v[S];
+#pragma unroll
+  for (int k = 0; k < S; ++k) v[k] = *reinterpret_cast<const float4*>(src + (size_t)k * rem * (kBM * kBN));
+  float4 acc = v[0];
+#pragma unroll
+  for (int k = 1; k < S; ++k) {
+    acc.x += v[k].x;
+    acc.y += v[k].y;
+    acc.z += v[k].z;
+    acc.w += v[k].w;
   }
   if (m >= M) return;
   const uint16_t o[4] = {__half_as_ushort(__float2half_rn(0.5f * acc.x)), __half_as_ushort(__float2half_rn(0.5f * acc.y)),
@@ -583,13 +589,19 @@ int64_t gemm_workspace_bytes(const GemmPlan& plan) {
 hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
                        int K, uint16_t* Y, float* part, const GemmPlan& plan, hipStream_t stream) {
   if (plan.small) return launch_gemm_small(Xq, sx, Wq, sw, M, N, K, Y, stream);
+  using Finish = void (*)(const float*, int, int, int, int, uint16_t*);
+  static constexpr Finish kFinish[kSplitMax + 1] = {
+      nullptr, nullptr, gemm_splitk_finish_kernel<2>, gemm_splitk_finish_kernel<3>, gemm_splitk_finish_kernel<4>,
+      gemm_splitk_finish_kernel<5>, gemm_splitk_finish_kernel<6>, gemm_splitk_finish_kernel<7>,
+      gemm_splitk_finish_kernel<8>};
+  if (plan.rem > 0 && (plan.splits < 2 || plan.splits > kSplitMax)) return hipErrorInvalidValue;
   const int blocks = plan.full + plan.rem * plan.splits;
   hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, false>), dim3(blocks),
                      dim3(kWavesM * kWavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr,
                      plan.full, plan.rem, plan.splits, part);
   if (plan.rem > 0)
-    hipLaunchKernelGGL(gemm_splitk_finish_kernel, dim3(kBM * kBN / 4 / 256, plan.rem), dim3(256), 0, stream, part,
-                       plan.full, plan.rem, plan.splits, M, N, Y);
+    hipLaunchKernelGGL(kFinish[plan.splits], dim3(kBM * kBN / 4 / 256, plan.rem), dim3(256), 0, stream, part,
+                       plan.full, plan.rem, M, N, Y);
   return hipGetLastError();
 }
 
