@@ -25,16 +25,23 @@
 // Exact codes without a per-element IEEE division: with r = 1/s correctly rounded,
 // t = x*r, e = fma(-t, s, x), u = fma(e, r, t), the integer nearest u (ties to even) equals
 // the integer nearest the correctly rounded fp32 quotient x/s for every fp16 x and every
-// fp16 scale s this rule can produce (checked over all 2.0e9 such pairs on the CPU).
-// Adding 1.5*2^23 rounds the clamped value (or its magnitude) to that integer with ties to
-// even and leaves its two's-complement low byte in the low bits of the sum.
+// fp16 scale s this rule can produce (checked over all 2.0e9 such pairs on the CPU).  The
+// scale itself and r come from a reciprocal and one correction step each, not from an IEEE
+// divide (exact for every fp16 input, see quantize16).  INT8 codes: adding 1.5*2^23 rounds
+// the clamped value to that integer with ties to even and leaves its two's-complement low
+// byte in the low bits of the sum.  INT4 codes: a mixed-precision fma rounds u + 1536 once
+// to fp16 (spacing 1 there), which after subtracting 1536 is the integer code as an fp16
+// value, +0 for a zero code.
 //
 // Packed INT4 layout (chosen so that a GEMM turns 16 codes into fp6 e2m3 MFMA operands with
 // four bit operations): a unit of 16 consecutive codes c0..c15 is 8 bytes.  Code c_i is the
 // fp6 e2m3 field f_i = |c_i| | (c_i < 0) << 5 (the subnormal c_i / 8) at bits 6i .. 6i+5 of a
 // 96-bit string T0:T1:T2; the exponent bits (3 and 4 of every field) are zero, and T2's bits
 // lie exactly at the exponent positions of T0 (kFp6Exp0) and T1 (kFp6Exp1), so the unit is
-// stored as the words T0 | (T2 & kFp6Exp0), T1 | (T2 & kFp6Exp1).
+// stored as the words T0 | (T2 & kFp6Exp0), T1 | (T2 & kFp6Exp1).  T0:T1:T2 is what
+// v_cvt_scalef32_pk32_fp6_f16 returns for the 16 fp16 codes with scale 8 (it rounds
+// value / scale to e2m3 to nearest even and packs value i at bits 6i; the codes are exact
+// there, and a zero code is +0, so no field reads as the negative zero 0x20).
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
@@ -85,6 +92,21 @@ __device__ __forceinline__ float code_value(_Float16 xh, float s, float r, float
 
 // Adding 1.5 * 2^23 rounds to an integer (ties to even) and leaves it in the low bits.
 constexpr float kRound = 12582912.0f;
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+
+// fp16 pair (rint(a) + 1536, rint(b) + 1536), each rounded once from the exact fp32 sum
+// (v_fma_mix computes a * 1 + 1536 unrounded and rounds to fp16, whose spacing is 1 on
+// [1024, 2048)): ties go to the even integer, as 1536 is even.  Subtracting 1536 afterwards
+// gives the integers exactly, with +0 for a zero code.
+__device__ __forceinline__ h2 round_pair_biased(float a, float b, float bias) {
+  uint32_t d;
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, %2\n\tv_fma_mixhi_f16 %0, %3, 1.0, %2" : "=&v"(d) : "v"(a), "s"(bias), "v"(b));
+  return __builtin_bit_cast(h2, d);
+}
+constexpr float kBias16 = 1536.0f;
 
 // low bytes of a,b,c,d -> one word [a, b, c, d]
 __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -162,33 +184,47 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
     const float a = group_max8((float)ah);
 
     const float qmax = tail ? 127.0f : 7.0f;
-    const __half s16 = __float2half_rn(a / qmax);      // correctly rounded fp32 divide, then RNE to fp16
+    // s = fp16_rne(fl32(a / qmax)) without a divide: q1 (the quotient through the rounded
+    // reciprocal, corrected once) can differ from the fp32 quotient, but never in its fp16
+    // rounding, for any fp16 a and either qmax (checked over all fp16 values on the CPU)
+    const float qinv = tail ? 1.0f / 127.0f : 1.0f / 7.0f;
+    const float q0 = a * qinv;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, qmax, a), qinv, q0);
+    const __half s16 = __float2half_rn(q1);
     const float s = __half2float(s16);
-    // s == 0 (an all-zero group, or a scale that underflows fp16): r = 0 makes every code 0,
-    // since then t = 0, e = x, u = 0 for the group's (zero) elements; no branch needed
-    const float r = s > 0.0f ? 1.0f / s : 0.0f;
+    // r = fl32(1 / s): the hardware reciprocal (within one ulp) refined by one Newton step is
+    // the correctly rounded reciprocal for every fp16 s > 0 (checked on the CPU for all three
+    // starting values within one ulp).  s == 0 (an all-zero group, or a scale that underflows
+    // fp16): r = 0 makes every code 0, since then t = 0, e = x, u = 0 for the group's (zero)
+    // elements; no branch needed
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    const float r = s > 0.0f ? __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0) : 0.0f;
     float v[kPerThread];
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) v[i] = code_value(x[i], s, r, qmax);
-    uint32_t b[kPerThread];                              // two's-complement code in the low byte
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) b[i] = __float_as_uint(v[i] + kRound);
     if (!tail) {
-      // INT4 unit: fp6 fields f_i at bits 6i of T0:T1:T2, T2 folded into the exponent bits
-      uint32_t f[kPerThread];
+      // INT4 unit: the integer codes as fp16, then one conversion to fp6 e2m3 with scale 8
+      // (code / 8, exact on the subnormal grid) that packs field i at bits 6i of T0:T1:T2; T2
+      // is then folded into the exponent bits of T0 and T1
+      h16 n;
 #pragma unroll
-      for (int i = 0; i < kPerThread; ++i) {
-        const uint32_t m = __float_as_uint(__builtin_fabsf(v[i]) + kRound) & 7u;   // |code|
-        f[i] = (b[i] & 0x20u) | m;   // bits 3-7 of a two's-complement code in [-7, 7] equal its sign
+      for (int i = 0; i < kPerThread; i += 2) {
+        const h2 p = round_pair_biased(v[i], v[i + 1], kBias16) - h2{(_Float16)kBias16, (_Float16)kBias16};
+        n[i] = p.x;
+        n[i + 1] = p.y;
       }
-      const uint32_t t0 = f[0] | f[1] << 6 | f[2] << 12 | f[3] << 18 | f[4] << 24 | f[5] << 30;
-      const uint32_t t1 = f[5] >> 2 | f[6] << 4 | f[7] << 10 | f[8] << 16 | f[9] << 22 | f[10] << 28;
-      const uint32_t t2 = f[10] >> 4 | f[11] << 2 | f[12] << 8 | f[13] << 14 | f[14] << 20 | f[15] << 26;
+      const u32x6 t = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(
+          __builtin_shufflevector(n, n, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, -1, -1, -1, -1, -1, -1,
+                                  -1, -1, -1, -1, -1, -1, -1, -1, -1, -1),
+          8.0f);
       uint2 w;
-      w.x = t0 | (t2 & kFp6Exp0);
-      w.y = t1 | (t2 & kFp6Exp1);
+      w.x = t[0] | (t[2] & kFp6Exp0);
+      w.y = t[1] | (t[2] & kFp6Exp1);
       *reinterpret_cast<uint2*>(qrow + c / 2) = w;
     } else {
+      uint32_t b[kPerThread];                            // two's-complement code in the low byte
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) b[i] = __float_as_uint(v[i] + kRound);
       u32x4 w;
       w.x = pack4(b[0], b[1], b[2], b[3]);
       w.y = pack4(b[4], b[5], b[6], b[7]);

@@ -112,6 +112,8 @@ int atom_pack_weights(const void *W, const int32_t *perm, int32_t N, int32_t K,
  *   code = 0 where s == 0.
  *   X    : const fp16 [M, K]      perm : const int32 [K]
  *   Xq   : uint8 [M, RB]          sx   : fp16 [G, M]           (outputs)
+ * Elements must be finite: a group holding an inf or NaN gets unspecified codes and scale
+ * (no fault).  The same holds for W in atom_pack_weights.
  */
 int atom_quantize_act(const void *X, const int32_t *perm, int32_t M, int32_t K,
                       void *Xq, void *sx, void *stream);

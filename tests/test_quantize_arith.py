@@ -1,0 +1,97 @@
+"""Exactness of the quantize kernel's division-free arithmetic, checked over every fp16 input.
+
+The activation quantize (quantization record of "Atom: Low-bit Quantization for Efficient and
+Accurate LLM Serving", Fields "Bits" and "Weight group size": per-group scale
+s = fp16(a / qmax) and codes rint(x / s)) avoids IEEE divides on the GPU:
+
+- the scale: q0 = fl(a * fl(1/qmax)), q1 = fma(fma(-q0, qmax, a), fl(1/qmax), q0); the kernel
+  stores fp16(q1), which must equal fp16(fl32(a / qmax));
+- the reciprocal: from any r0 within one ulp of 1/s (the hardware reciprocal's accuracy),
+  fma(fma(-s, r0, 1), r0, r0) must be the correctly rounded fl32(1 / s);
+- the INT4 code: fp16(u + 1536), rounded once from the exact sum, minus 1536, must be the
+  integer nearest u with ties to even.
+
+Every claim is checked with exact rational arithmetic: fp32 and fp16 rounding are written out
+here (round to nearest, ties to even), the fused operations round once.
+"""
+from fractions import Fraction as F
+import struct
+
+import numpy as np
+import pytest
+
+
+def _round(q, mant_bits):
+    """q rounded to a binary float with mant_bits fraction bits, nearest, ties to even
+    (normal range only; every value below stays in it)."""
+    if q == 0:
+        return F(0)
+    sign = -1 if q < 0 else 1
+    q = abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    if F(2) ** e > q:
+        e -= 1
+    m = q * F(2) ** (mant_bits - e)
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > F(1, 2) or (rem == F(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * F(fl) * F(2) ** (e - mant_bits)
+
+
+def rn32(q):
+    return _round(q, 23)
+
+
+def fp16_bits(q):
+    """fp16 bits of a value that is already an fp32 value (numpy rounds to nearest even)."""
+    return int(np.float16(np.float32(float(q))).view(np.uint16))
+
+
+def f32_step(q, d):
+    b = struct.unpack("<I", struct.pack("<f", float(q)))[0] + d
+    return F(struct.unpack("<f", struct.pack("<I", b))[0])
+
+
+POSITIVE_FP16 = [F(float(h)) for h in np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16)]
+
+
+@pytest.mark.parametrize("qmax", [7, 127])
+def test_scale_without_divide_matches_fp16_of_fp32_quotient(qmax):
+    c = rn32(F(1, qmax))
+    bad = []
+    for a in POSITIVE_FP16:
+        q0 = rn32(a * c)
+        q1 = rn32(rn32(a - q0 * qmax) * c + q0)
+        if fp16_bits(q1) != fp16_bits(rn32(a / qmax)):
+            bad.append(float(a))
+    assert not bad, bad[:10]
+
+
+def test_refined_reciprocal_is_correctly_rounded():
+    bad = []
+    for s in POSITIVE_FP16:
+        exact = rn32(1 / s)
+        for r0 in (f32_step(exact, -1), exact, f32_step(exact, 1)):
+            r1 = rn32(rn32(1 - s * r0) * r0 + r0)
+            if r1 != exact:
+                bad.append((float(s), float(r0)))
+    assert not bad, bad[:10]
+
+
+def test_biased_fp16_rounding_gives_integer_code_ties_to_even():
+    # every half-integer in [-7.5, 7.5], its fp32 neighbours, and a spread of other values
+    vals = []
+    for k in range(-15, 16):
+        h = F(k, 2)
+        vals.append(h)
+        vals.append(f32_step(h, 1) if h > 0 else f32_step(h, -1) if h < 0 else F(2) ** -149)
+        if h != 0:
+            vals.append(f32_step(h, -1) if h > 0 else f32_step(h, 1))
+    vals += [F(i, 64) for i in range(-7 * 64, 7 * 64 + 1)]
+    for u in vals:
+        n = _round(u + 1536, 10) - 1536        # fp16 has 10 fraction bits; spacing 1 on [1024, 2048)
+        fl = u.numerator // u.denominator
+        rem = u - fl
+        want = fl + 1 if rem > F(1, 2) or (rem == F(1, 2) and fl % 2 == 1) else fl
+        assert n == want, (float(u), n, want)
