@@ -79,6 +79,17 @@ def traffic_for_current_gemm():
     return d.get("bytes_per_launch_by_workload")
 
 
+def traffic_for_current_quantize():
+    """HBM bytes per 8192 x 8192 quantize launch from the same counter summary, only while the
+    quantize source is unchanged since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    d = json.load(open(TRAFFIC_FILE))
+    if d.get("quantize_source_sha256") != sha256(QUANT_SRC):
+        return None
+    return d.get("quantize_8192_bytes_per_launch")
+
+
 class _nullctx:
     def __enter__(self):
         return self
@@ -164,7 +175,8 @@ def quant_only(args, torch, bq, synth, dev, R):
         "dtype": "fp16->int4/int8", "data": "synthetic",
         "config": {"workload": "quantize_only_8192x8192", "M": M, "K": K, "rotating_input_copies": R},
         "roofline": {"kernel": "row_quantize_kernel", "bound": "hbm", "achieved": round(gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for_current_quantize() if (M, K) == (8192, 8192) else None,
                      "bytes_per_launch": qb, "avg_launch_us": round(ms * 1e3, 3)},
     }
     print(json.dumps(line), flush=True)
