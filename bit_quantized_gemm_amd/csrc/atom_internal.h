@@ -30,8 +30,8 @@ struct GemmPlan {
   int full, rem, splits;
   int small;
 };
-// Few-rows kernel: at most kSmallMaxM token rows, at most kSmallMaxGroups INT4 groups per K range.
-constexpr int kSmallMaxM = 16, kSmallMaxGroups = 4;
+// Few-rows kernel: at most kSmallMaxM token rows.
+constexpr int kSmallMaxM = 16;
 GemmPlan gemm_plan(int M, int N, int K);
 // Scratch bytes the plan needs (0 when it writes Y directly).
 int64_t gemm_workspace_bytes(const GemmPlan& plan);

@@ -8,10 +8,10 @@
 // reading the packed weights once from HBM; 128 x 128 tiles would waste 7/8 of every MFMA and
 // leave the copies latency-bound.
 //
-// Work layout.  A workgroup owns 16 output columns.  K is cut into ranges of at most
-// kSmallMaxGroups INT4 groups (the last range also takes the INT8 outlier group); the
-// workgroup has one wave per range, at most 16, and a wave takes every 16th range when there
-// are more.  A wave issues every load of a range at once straight into registers (no LDS
+// Work layout.  A workgroup owns 16 output columns.  K is cut into ranges of at most MAXG
+// INT4 groups (the last range also takes the INT8 outlier group): 4, or 6 when ranges of 4
+// would need more than 16 waves; the workgroup has one wave per range, at most 16, and a wave
+// takes every 16th range when there are more.  A wave issues every load of a range at once straight into registers (no LDS
 // staging, no barrier), then runs one 16 x 16 x 128 fp6 MFMA per group.  At the end the waves'
 // fp32 sums meet in LDS and wave 0 adds them in wave order and writes Y: one kernel, no
 // scratch, deterministic.
@@ -68,6 +68,7 @@ __device__ __forceinline__ h4 scale_operand(uint16_t v) {
 constexpr int kMaxWaves = 16;                // waves (K ranges in flight) per workgroup
 
 // blockIdx.x: column block (columns n0 = 16 blockIdx.x ..); wave w handles K ranges w, w + waves, ...
+template <int MAXG>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const uint8_t* __restrict__ Xq,
                                                                          const uint16_t* __restrict__ sx,
                                                                          const uint8_t* __restrict__ Wq,
@@ -87,17 +88,17 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
 
   v4f yacc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int range = wave; range < ranges; range += waves) {
-    const int ga = range * (G - 1) / ranges, gb = (range + 1) * (G - 1) / ranges;   // 1 .. kSmallMaxGroups
+    const int ga = range * (G - 1) / ranges, gb = (range + 1) * (G - 1) / ranges;   // 1 .. MAXG
     const int ng = gb - ga;                                                         // uniform
     const bool last = range == ranges - 1;                                          // uniform
     // Every load of the range is issued, unconditionally, before any of it is used (a load
     // under a branch would first wait for all earlier ones).  Groups past the range's end
     // repeat its last group, and outside the last range the INT8 group's loads repeat group
     // ga's bytes and scales: in bounds, cached, never used.
-    uint4 wl[kSmallMaxGroups], xl[kSmallMaxGroups];
-    uint16_t wsc[kSmallMaxGroups], xsc[kSmallMaxGroups];
+    uint4 wl[MAXG], xl[MAXG];
+    uint16_t wsc[MAXG], xsc[MAXG];
 #pragma unroll
-    for (int i = 0; i < kSmallMaxGroups; ++i) {
+    for (int i = 0; i < MAXG; ++i) {
       const int g = min(ga + i, gb - 1);
       wl[i] = *reinterpret_cast<const uint4*>(wrow + (size_t)g * 64);
       xl[i] = *reinterpret_cast<const uint4*>(xrow + (size_t)g * 64);
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
     // Branch-free as well (a load used only under a branch gets sunk into it): a repeated
     // group gets a zero scale product and adds exactly +0.
 #pragma unroll
-    for (int i = 0; i < kSmallMaxGroups; ++i) {
+    for (int i = 0; i < MAXG; ++i) {
       const v8i a = fp6_operand(wl[i]);
       const v8i b = fp6_operand(xl[i]);
       // cbsz = blgp = 2: both operands fp6 e2m3
@@ -168,10 +169,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
 hipError_t launch_gemm_small(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M,
                              int N, int K, uint16_t* Y, hipStream_t stream) {
   const int G = K / ATOM_GROUP;
-  const int ranges = (G - 1 + kSmallMaxGroups - 1) / kSmallMaxGroups;
+  // Ranges of 4 groups while they fit one wave each; beyond 16 ranges, ranges of 6 (fewer
+  // waves that take a second range).  Measured on 16-token batches (event-timed): 16 x 11008
+  // x 4096 (85 INT4 groups) 11.3 -> 10.7 us with ranges of 6; with 31 INT4 groups ranges of 6
+  // are slower (16 x 4096 x 11008: 11.1 -> 11.4 us), and ranges of 2 are slower everywhere.
+  const bool wide = (G - 1 + 3) / 4 > kMaxWaves;
+  const int maxg = wide ? 6 : 4;
+  const int ranges = (G - 1 + maxg - 1) / maxg;
   const int waves = ranges < kMaxWaves ? ranges : kMaxWaves;
-  hipLaunchKernelGGL(gemm_w4a4_small_kernel, dim3((N + kCols - 1) / kCols), dim3(64 * waves), 0, stream, Xq, sx, Wq,
-                     sw, M, N, K, ranges, Y);
+  const dim3 grid((N + kCols - 1) / kCols), block(64 * waves);
+  if (wide)
+    hipLaunchKernelGGL(gemm_w4a4_small_kernel<6>, grid, block, 0, stream, Xq, sx, Wq, sw, M, N, K, ranges, Y);
+  else
+    hipLaunchKernelGGL(gemm_w4a4_small_kernel<4>, grid, block, 0, stream, Xq, sx, Wq, sw, M, N, K, ranges, Y);
   return hipGetLastError();
 }
 
