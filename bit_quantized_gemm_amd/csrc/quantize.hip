@@ -293,22 +293,34 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
   }
 }
 
+// Resident workgroups of one instantiation: per compute unit (for its largest row's LDS) and
+// the compute-unit count, queried on the current device.
+struct Residency {
+  int per_cu, cus;
+};
+
+template <int CHUNKS, int PASSES>
+Residency query_residency() {
+  Residency r{2, 256};                               // fallbacks if a query fails
+  int dev = 0, n = 0, b = 0;
+  if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      n > 0)
+    r.cus = n;
+  const size_t lds_max = (size_t)staged_stride(CHUNKS * 8 * kThreads) * 8 * sizeof(uint32_t);   // largest row of this range
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, row_quantize_kernel<CHUNKS, PASSES>, kThreads, lds_max) ==
+          hipSuccess && b > 0)
+    r.per_cu = b;
+  return r;
+}
+
 template <int CHUNKS, int PASSES>
 hipError_t launch_rq(const uint16_t* X, const int32_t* perm, int rows, int K, uint8_t* Q, uint16_t* S,
                      hipStream_t stream) {
   const size_t lds = (size_t)staged_stride(K) * 8 * sizeof(uint32_t);
-  static int per_cu = 0, cus = 0;                   // occupancy of this instantiation, filled on first use
-  if (per_cu == 0) {
-    int dev = 0, n = 0, b = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-      cus = n;
-    const size_t lds_max = (size_t)staged_stride(CHUNKS * 8 * kThreads) * 8 * sizeof(uint32_t);   // largest row of this range
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, row_quantize_kernel<CHUNKS, PASSES>, kThreads, lds_max) ==
-            hipSuccess && b > 0)
-      per_cu = b;
-    if (cus <= 0) cus = 256;
-    if (per_cu <= 0) per_cu = 2;
-  }
+  // queried once per process and instantiation (the initialisation of a function-local static
+  // is thread-safe), on the device current at the first call
+  static const Residency res = query_residency<CHUNKS, PASSES>();
+  const int per_cu = res.per_cu, cus = res.cus;
   const int lim = per_cu * cus;
   // passes of a row as separate items when the rows alone leave resident slots empty
   const int passes = (K + kThreads * kPerThread - 1) / (kThreads * kPerThread);
