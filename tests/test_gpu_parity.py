@@ -286,7 +286,10 @@ def test_deterministic_and_side_stream():
 
 
 # --------------------------------------------------------------------------- split-K (atom_gemm_ws)
-SPLIT = [(64, 128, 4096), (200, 300, 2048), (17, 130, 1152), (256, 4096, 4096)]
+# pieces per split tile: 7, 3, 2, 4 (the Llama-7B attention projection), 5, 6, 8; every piece count
+# has its own finalize instance
+SPLIT = [(64, 128, 4096), (200, 300, 2048), (17, 130, 1152), (256, 4096, 4096), (17, 64, 3072), (40, 200, 3456),
+         (33, 250, 4352)]
 
 
 @pytest.mark.parametrize("M,N,K", SPLIT)
