@@ -36,6 +36,11 @@ Readings taken where the pages are silent (each one is also a parameter of the H
   are always zero for these codes (see ``pack_rows``); the 128 INT8 outlier codes are
   appended as the last 128 two's-complement bytes of each row;
 * output: ``Y = sum_g acc_g * sx_g * sw_g`` rounded once to fp16 (round to nearest even).
+
+W4A8 variant (a next step beside the path; the pages point to it only as the precision another
+method's kernels target): activations get INT8 codes in every group (same scale rule with
+qmax = 127, one byte per code), weights keep the W4 rule and are packed as offset-binary
+nibbles (``pack_rows_w4a8``); the group products and the output are the same definitions.
 """
 from __future__ import annotations
 
@@ -99,12 +104,13 @@ def outlier_perm(X_calib: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------- step: quantize one row set
-def quantize_rows(X: np.ndarray, perm: np.ndarray):
+def quantize_rows(X: np.ndarray, perm: np.ndarray, all_int8: bool = False):
     """Reorder the columns of fp16 ``X`` [rows, K] through ``perm`` and quantize each
     128-wide group of each row independently.
 
     Returns ``(codes int8 [rows, K], scales fp16 [G, rows])``: groups 0..G-2 hold INT4
     codes in [-7, 7], group G-1 (the 128 outlier channels) holds INT8 codes in [-127, 127].
+    With ``all_int8`` (the W4A8 variant's activations) every group holds INT8 codes.
     """
     X = np.asarray(X)
     if X.dtype != np.float16:
@@ -114,7 +120,7 @@ def quantize_rows(X: np.ndarray, perm: np.ndarray):
     perm = np.asarray(perm, dtype=np.int64)
     xr = X[:, perm].astype(np.float32).reshape(rows, G, GROUP)     # fp16 -> fp32 is exact
 
-    qmax = np.full(G, QMAX_INT4, dtype=np.float32)
+    qmax = np.full(G, QMAX_INT8 if all_int8 else QMAX_INT4, dtype=np.float32)
     qmax[G - 1] = QMAX_INT8
     a = np.max(np.abs(xr), axis=2)                                   # group absmax (exact)
     s32 = a / qmax[None, :]                                          # IEEE fp32 division
@@ -194,6 +200,67 @@ def unpack_rows(packed: np.ndarray, K: int) -> np.ndarray:
     out[:, :klo] = np.where(neg == 1, -mag, mag).reshape(rows, klo)
     out[:, klo:] = packed[:, klo // 2:].view(np.int8)
     return out
+
+
+# --------------------------------------------------------------------------- W4A8 variant: layouts
+def pack_rows_a8(codes: np.ndarray) -> np.ndarray:
+    """INT8 activation codes [rows, K] -> bytes [rows, K]: each code as one two's-complement
+    byte, in reordered channel order."""
+    codes = np.asarray(codes, dtype=np.int8)
+    return np.ascontiguousarray(codes).view(np.uint8).copy()
+
+
+def unpack_rows_a8(packed: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of :func:`pack_rows_a8`."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    assert packed.shape[1] == K
+    return packed.view(np.int8).copy()
+
+
+def pack_rows_w4a8(codes: np.ndarray) -> np.ndarray:
+    """W4 codes [rows, K] (INT4 in groups 0..G-2, INT8 in group G-1) -> bytes
+    [rows, (K-128)/2 + 128] for the W4A8 GEMM.
+
+    The K-128 INT4 codes go in blocks of 8 consecutive codes c_0..c_7, each block 4 bytes:
+    byte j (j = 0..3) holds c_j + 8 in its low nibble and c_{j+4} + 8 in its high nibble
+    (offset binary, values 1..15).  Masking a little-endian word with 0x0F0F0F0F gives the
+    biased codes c_0..c_3 as bytes, shifting it right by 4 first gives c_4..c_7.  The 128
+    INT8 codes follow as two's-complement bytes."""
+    codes = np.asarray(codes, dtype=np.int8)
+    rows, K = codes.shape
+    klo = K - OUTLIERS
+    q = codes[:, :klo].astype(np.int16) + 8
+    if q.min(initial=8) < 1 or q.max(initial=8) > 15:
+        raise ValueError("INT4 codes must lie in [-7, 7]")
+    blk = q.reshape(rows, klo // 8, 8)
+    body = (blk[:, :, :4] | (blk[:, :, 4:] << 4)).astype(np.uint8).reshape(rows, klo // 2)
+    tail = np.ascontiguousarray(codes[:, klo:]).view(np.uint8)
+    return np.ascontiguousarray(np.concatenate([body, tail], axis=1))
+
+
+def unpack_rows_w4a8(packed: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of :func:`pack_rows_w4a8`."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    rows = packed.shape[0]
+    klo = K - OUTLIERS
+    body = packed[:, :klo // 2].reshape(rows, klo // 8, 4).astype(np.int16)
+    lo, hi = body & 0xF, body >> 4
+    q = (np.concatenate([lo, hi], axis=2) - 8).reshape(rows, klo).astype(np.int8)
+    tail = packed[:, klo // 2:].view(np.int8)
+    return np.concatenate([q, tail], axis=1)
+
+
+def quantize_act_a8(X: np.ndarray, perm: np.ndarray):
+    """W4A8 runtime activation quantize: (bytes u8 [M, K], scales fp16 [G, M])."""
+    q, s = quantize_rows(X, perm, all_int8=True)
+    return pack_rows_a8(q), s
+
+
+def pack_weights_w4a8(W: np.ndarray, perm: np.ndarray):
+    """W4A8 offline weight pack: the W4 rule, offset-binary layout (u8 [N, row_bytes],
+    scales fp16 [G, N])."""
+    q, s = quantize_rows(W, perm)
+    return pack_rows_w4a8(q), s
 
 
 # --------------------------------------------------------------------------- the layer's two runtime calls
