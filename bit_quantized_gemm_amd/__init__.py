@@ -13,6 +13,8 @@ The function names are the C entry points:
 * ``atom_quantize_act(X, perm)``          -> (Xq u8 [M, RB], sx fp16 [G, M])
 * ``atom_gemm(Xq, sx, Wq, sw, K)``        -> Y fp16 [M, N]
 * ``atom_gemm_group_acc(Xq, Wq, K)``      -> acc int32 [G, M, N]   (verification aid)
+* W4A8 variant: ``atom_quantize_act_a8(X, perm)`` -> (Xq u8 [M, K], sx), ``atom_pack_weights_w4a8(W, perm)``
+  -> (Wq u8 [N, RB], sw), ``atom_gemm_w4a8(Xq, sx, Wq, sw, K)`` -> Y, ``atom_gemm_w4a8_group_acc(Xq, Wq, K)``
 * ``atom_row_bytes(K)``, ``atom_num_groups(K)``, ``atom_strerror(status)``
 """
 from __future__ import annotations
@@ -24,7 +26,8 @@ __all__ = [
     "AtomError", "EXPORTS", "GROUP", "OUTLIERS", "MAX_K", "lib_path", "load_library",
     "atom_row_bytes", "atom_num_groups", "atom_strerror", "atom_channel_stat", "atom_select_outliers",
     "atom_pack_weights", "atom_quantize_act", "atom_gemm", "atom_gemm_workspace_bytes", "atom_gemm_ws",
-    "atom_gemm_group_acc", "linear",
+    "atom_gemm_group_acc", "linear", "atom_quantize_act_a8", "atom_pack_weights_w4a8", "atom_gemm_w4a8",
+    "atom_gemm_w4a8_group_acc",
 ]
 
 GROUP = 128
@@ -35,7 +38,8 @@ MAX_K = 32768
 EXPORTS = (
     "atom_row_bytes", "atom_num_groups", "atom_strerror", "atom_channel_stat", "atom_select_outliers",
     "atom_pack_weights", "atom_quantize_act", "atom_gemm", "atom_gemm_workspace_bytes", "atom_gemm_ws",
-    "atom_gemm_group_acc",
+    "atom_gemm_group_acc", "atom_quantize_act_a8", "atom_pack_weights_w4a8", "atom_gemm_w4a8",
+    "atom_gemm_w4a8_group_acc",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +76,10 @@ def load_library():
         "atom_gemm_workspace_bytes": (i64, [i32, i32, i32]),
         "atom_gemm_ws": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp, i64, vp]),
         "atom_gemm_group_acc": (ctypes.c_int, [vp, vp, i32, i32, i32, vp, vp]),
+        "atom_quantize_act_a8": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp]),
+        "atom_pack_weights_w4a8": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp]),
+        "atom_gemm_w4a8": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp]),
+        "atom_gemm_w4a8_group_acc": (ctypes.c_int, [vp, vp, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -245,3 +253,55 @@ def linear(X, perm, Wq, sw, Y=None, stream=None, workspace=None):
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     return atom_gemm_ws(Xq, sx, Wq, sw, K, workspace if need else None, Y=Y, stream=stream)
+
+
+# --------------------------------------------------------------------------- W4A8 variant
+def atom_quantize_act_a8(X, perm, Xq=None, sx=None, stream=None):
+    """INT8 codes in every group: (Xq u8 [M, K], sx fp16 [G, M])."""
+    torch = _torch()
+    M, K = X.shape
+    _, sx = _rows_out(M, K, X, torch.empty(0), sx)
+    if Xq is None:
+        Xq = _empty((M, K), torch.uint8, X)
+    st = load_library().atom_quantize_act_a8(_dev(X, "X", torch.float16), _dev(perm, "perm", torch.int32), M, K,
+                                             _dev(Xq, "Xq", torch.uint8), _dev(sx, "sx", torch.float16),
+                                             _stream(stream, X.device))
+    _check(st, "atom_quantize_act_a8")
+    return Xq, sx
+
+
+def atom_pack_weights_w4a8(W, perm, Wq=None, sw=None, stream=None):
+    """W4 rule, offset-binary INT4 layout for the W4A8 GEMM: (Wq u8 [N, RB], sw fp16 [G, N])."""
+    torch = _torch()
+    N, K = W.shape
+    Wq, sw = _rows_out(N, K, W, Wq, sw)
+    st = load_library().atom_pack_weights_w4a8(_dev(W, "W", torch.float16), _dev(perm, "perm", torch.int32), N, K,
+                                               _dev(Wq, "Wq", torch.uint8), _dev(sw, "sw", torch.float16),
+                                               _stream(stream, W.device))
+    _check(st, "atom_pack_weights_w4a8")
+    return Wq, sw
+
+
+def atom_gemm_w4a8(Xq, sx, Wq, sw, K, Y=None, stream=None):
+    torch = _torch()
+    M = Xq.shape[0]
+    N = Wq.shape[0]
+    if Y is None:
+        Y = _empty((M, N), torch.float16, Xq)
+    st = load_library().atom_gemm_w4a8(_dev(Xq, "Xq", torch.uint8), _dev(sx, "sx", torch.float16),
+                                       _dev(Wq, "Wq", torch.uint8), _dev(sw, "sw", torch.float16), M, N, K,
+                                       _dev(Y, "Y", torch.float16), _stream(stream, Xq.device))
+    _check(st, "atom_gemm_w4a8")
+    return Y
+
+
+def atom_gemm_w4a8_group_acc(Xq, Wq, K, acc=None, stream=None):
+    torch = _torch()
+    M = Xq.shape[0]
+    N = Wq.shape[0]
+    if acc is None:
+        acc = _empty((K // GROUP, M, N), torch.int32, Xq)
+    st = load_library().atom_gemm_w4a8_group_acc(_dev(Xq, "Xq", torch.uint8), _dev(Wq, "Wq", torch.uint8), M, N, K,
+                                                 _dev(acc, "acc", torch.int32), _stream(stream, Xq.device))
+    _check(st, "atom_gemm_w4a8_group_acc")
+    return acc

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libatom.so")
 
-SOURCES = ["atom_api.cpp", "select.hip", "quantize.hip", "gemm.hip", "gemm_small.hip"]
+SOURCES = ["atom_api.cpp", "select.hip", "quantize.hip", "gemm.hip", "gemm_small.hip", "gemm_w4a8.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

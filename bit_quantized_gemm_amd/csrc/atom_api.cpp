@@ -45,12 +45,13 @@ int check_overlap(const Range* in, int n_in, const Range* out, int n_out) {
   return ATOM_OK;
 }
 
-int check_row_quantize(const void* X, const int32_t* perm, int32_t rows, int32_t K, void* Q, void* S) {
+// rb = bytes of one packed output row (W4A4 and W4A8 weights: (K-128)/2 + 128; A8: K)
+int check_row_quantize(const void* X, const int32_t* perm, int32_t rows, int32_t K, void* Q, void* S, bool a8) {
   if (!X || !perm || !Q || !S) return ATOM_E_NULL;
   if (!valid_k(K) || !valid_rows(rows)) return ATOM_E_SHAPE;
   if (!aligned16(X) || !aligned16(perm) || !aligned16(Q) || !aligned16(S)) return ATOM_E_ALIGN;
   const uint64_t G = (uint64_t)K / ATOM_GROUP;
-  const uint64_t rb = (uint64_t)atom_row_bytes(K);
+  const uint64_t rb = a8 ? (uint64_t)K : (uint64_t)atom_row_bytes(K);
   const Range in[2] = {range_of(X, (uint64_t)rows * K * 2), range_of(perm, (uint64_t)K * 4)};
   const Range out[2] = {range_of(Q, (uint64_t)rows * rb), range_of(S, G * rows * 2)};
   return check_overlap(in, 2, out, 2);
@@ -104,16 +105,16 @@ int atom_select_outliers(const double* stat, int32_t K, int32_t* perm, void* str
 }
 
 int atom_pack_weights(const void* W, const int32_t* perm, int32_t N, int32_t K, void* Wq, void* sw, void* stream) {
-  if (int s = check_row_quantize(W, perm, N, K, Wq, sw)) return s;
+  if (int s = check_row_quantize(W, perm, N, K, Wq, sw, false)) return s;
   return hip_status(atom::launch_row_quantize(static_cast<const uint16_t*>(W), perm, N, K,
-                                              static_cast<uint8_t*>(Wq), static_cast<uint16_t*>(sw),
+                                              static_cast<uint8_t*>(Wq), static_cast<uint16_t*>(sw), atom::kRowW4A4,
                                               static_cast<hipStream_t>(stream)));
 }
 
 int atom_quantize_act(const void* X, const int32_t* perm, int32_t M, int32_t K, void* Xq, void* sx, void* stream) {
-  if (int s = check_row_quantize(X, perm, M, K, Xq, sx)) return s;
+  if (int s = check_row_quantize(X, perm, M, K, Xq, sx, false)) return s;
   return hip_status(atom::launch_row_quantize(static_cast<const uint16_t*>(X), perm, M, K,
-                                              static_cast<uint8_t*>(Xq), static_cast<uint16_t*>(sx),
+                                              static_cast<uint8_t*>(Xq), static_cast<uint16_t*>(sx), atom::kRowW4A4,
                                               static_cast<hipStream_t>(stream)));
 }
 
@@ -164,6 +165,60 @@ int atom_gemm_group_acc(const void* Xq, const void* Wq, int32_t M, int32_t N, in
   if (int s = check_overlap(in, 2, out, 1)) return s;
   return hip_status(atom::launch_gemm_group_acc(static_cast<const uint8_t*>(Xq), static_cast<const uint8_t*>(Wq), M,
                                                 N, K, acc, static_cast<hipStream_t>(stream)));
+}
+
+// ---- W4A8 variant
+
+int atom_quantize_act_a8(const void* X, const int32_t* perm, int32_t M, int32_t K, void* Xq, void* sx,
+                         void* stream) {
+  if (int s = check_row_quantize(X, perm, M, K, Xq, sx, true)) return s;
+  return hip_status(atom::launch_row_quantize(static_cast<const uint16_t*>(X), perm, M, K,
+                                              static_cast<uint8_t*>(Xq), static_cast<uint16_t*>(sx), atom::kRowA8,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int atom_pack_weights_w4a8(const void* W, const int32_t* perm, int32_t N, int32_t K, void* Wq, void* sw,
+                           void* stream) {
+  if (int s = check_row_quantize(W, perm, N, K, Wq, sw, false)) return s;
+  return hip_status(atom::launch_row_quantize(static_cast<const uint16_t*>(W), perm, N, K,
+                                              static_cast<uint8_t*>(Wq), static_cast<uint16_t*>(sw), atom::kRowW4A8,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+static int w4a8_common(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N,
+                       int32_t K, void* Y, int32_t* acc, void* stream) {
+  const bool want_acc = acc != nullptr;
+  if (!Xq || !Wq || (want_acc ? false : (!sx || !sw || !Y))) return ATOM_E_NULL;
+  if (!valid_gemm(M, N, K)) return ATOM_E_SHAPE;
+  if (!aligned16(Xq) || !aligned16(Wq)) return ATOM_E_ALIGN;
+  if (!want_acc && (!aligned16(sx) || !aligned16(sw) || !aligned16(Y))) return ATOM_E_ALIGN;
+  if (want_acc && !aligned16(acc)) return ATOM_E_ALIGN;
+  const uint64_t G = (uint64_t)K / ATOM_GROUP;
+  const uint64_t rbw = (uint64_t)atom_row_bytes(K);
+  if (want_acc) {
+    const Range in[2] = {range_of(Xq, (uint64_t)M * K), range_of(Wq, (uint64_t)N * rbw)};
+    const Range out[1] = {range_of(acc, G * M * N * 4)};
+    if (int s = check_overlap(in, 2, out, 1)) return s;
+  } else {
+    const Range in[4] = {range_of(Xq, (uint64_t)M * K), range_of(sx, G * M * 2), range_of(Wq, (uint64_t)N * rbw),
+                         range_of(sw, G * N * 2)};
+    const Range out[1] = {range_of(Y, (uint64_t)M * N * 2)};
+    if (int s = check_overlap(in, 4, out, 1)) return s;
+  }
+  return hip_status(atom::launch_gemm_w4a8(static_cast<const uint8_t*>(Xq), static_cast<const uint16_t*>(sx),
+                                           static_cast<const uint8_t*>(Wq), static_cast<const uint16_t*>(sw), M, N,
+                                           K, static_cast<uint16_t*>(Y), acc, static_cast<hipStream_t>(stream)));
+}
+
+int atom_gemm_w4a8(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N, int32_t K,
+                   void* Y, void* stream) {
+  return w4a8_common(Xq, sx, Wq, sw, M, N, K, Y, nullptr, stream);
+}
+
+int atom_gemm_w4a8_group_acc(const void* Xq, const void* Wq, int32_t M, int32_t N, int32_t K, int32_t* acc,
+                             void* stream) {
+  if (!acc) return ATOM_E_NULL;
+  return w4a8_common(Xq, nullptr, Wq, nullptr, M, N, K, nullptr, acc, stream);
 }
 
 }  // extern "C"

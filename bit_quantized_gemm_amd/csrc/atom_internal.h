@@ -19,8 +19,14 @@ constexpr uint32_t kFp6Exp0 = 0x18618618u, kFp6Exp1 = 0x86186186u;
 
 hipError_t launch_channel_stat(const uint16_t* X, int M, int K, double* stat, hipStream_t stream);
 hipError_t launch_select_outliers(const double* stat, int K, int32_t* perm, hipStream_t stream);
+// Packed row formats the row quantize writes.
+//   kRowW4A4: INT4 groups in the fp6-fold units above, INT8 outlier group last; (K-128)/2 + 128 bytes.
+//   kRowA8:   every group INT8 (qmax 127), one two's-complement byte per code; K bytes.
+//   kRowW4A8: INT4 groups as offset-binary nibbles (byte j of each 8-code block holds c_j + 8
+//             and c_{j+4} + 8 in its low and high nibble), INT8 outlier group last; (K-128)/2 + 128 bytes.
+enum RowFormat { kRowW4A4 = 0, kRowA8 = 1, kRowW4A8 = 2 };
 hipError_t launch_row_quantize(const uint16_t* X, const int32_t* perm, int rows, int K, uint8_t* Q,
-                               uint16_t* S, hipStream_t stream);
+                               uint16_t* S, RowFormat fmt, hipStream_t stream);
 // Split-K plan of a GEMM: the first `full` output tiles (in the kernel's tile order) run whole;
 // each of the last `rem` tiles is divided into `splits` pieces along K, whose fp32 partial
 // tiles go to caller scratch and are added by a second kernel.  rem == 0: no split.  The
@@ -43,5 +49,9 @@ hipError_t launch_gemm_small(const uint8_t* Xq, const uint16_t* sx, const uint8_
                              int N, int K, uint16_t* Y, hipStream_t stream);
 hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K, int32_t* acc,
                                  hipStream_t stream);
+// W4A8 GEMM (gemm_w4a8.hip): Xq in kRowA8 rows, Wq in kRowW4A8 rows.  acc != nullptr: write
+// the per-group int32 accumulators [G, M, N] instead of Y.
+hipError_t launch_gemm_w4a8(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M,
+                            int N, int K, uint16_t* Y, int32_t* acc, hipStream_t stream);
 
 }  // namespace atom

@@ -1,0 +1,280 @@
+// W4A8 GEMM for gfx950: INT8 activation codes in every 128-channel group against the W4
+// weights (INT4 bulk, INT8 outlier group), a variant beside the W4A4 path.
+//
+// Y[m,n] = sum over groups g of acc_g[m,n] * sx[g,m] * sw[g,n], acc_g the exact integer dot
+// product of the codes of group g, as for W4A4 (quantization record of "Atom (mixed-precision
+// block-outlier low-bit quantization for serving)", Fields "Bits", "Weight group size",
+// "notes": per-group scales, the 128-channel INT8 group).  INT8 activation codes are not exact
+// fp6 or fp8 values, so every group runs on v_mfma_i32_32x32x32_i8.
+//
+// Operands.  Activation rows are K two's-complement bytes; a lane's 16 bytes of a K = 32 slice
+// feed the MFMA as they are.  Weight rows keep the INT4 groups as offset-binary nibbles (byte j
+// of each 8-code block holds c_j + 8 and c_{j+4} + 8): for 16 consecutive codes (two words
+// w0, w1) the int8 operand is {w0 & 0x0F0F0F0F, (w0 >> 4) & 0x0F0F0F0F, w1 & .., (w1 >> 4) & ..},
+// the biased codes c + 8 in order.  The MFMA then sums a * (c + 8); one more MFMA per K slice
+// with the constant -8 as weight operand puts -8 * sum(a) into the accumulator first, so the
+// result is the exact sum of a * c.  The INT8 outlier group's weights are two's-complement
+// bytes and need no correction.  Every partial sum is an integer below 2^31.
+//
+// K slices.  In a K = 32 slice t of a group, lane l supplies row (activations: token; weights:
+// output column) l & 31 and the 16 codes 32 t + 16 (l >> 5) .. + 15; both operands use the same
+// assignment, so every code of the group meets its partner once.  The weights are the first
+// operand, so a 32x32 accumulator holds its output tile transposed: lane l owns output row
+// l & 31, element r is column (r >> 2) * 8 + (l >> 5) * 4 + (r & 3).
+//
+// Scales and epilogue.  As in the W4A4 kernel: one v_mfma_f32_32x32x8_f16 with each lane's
+// fp16 scale in K slot 0 of its half gives 2 * sx * sw exactly in the accumulator layout, the
+// int32 group sum is converted (exact below 2^24 .. here below 2^21) and added with one fp32 fma
+// per element and group; the factor 2 goes at the store.
+//
+// Work layout.  One workgroup of 4 waves per 128 x 128 output tile (2 x 2 waves of 64 x 64,
+// each 2 x 2 MFMA tiles).  Per group the activation stage (128 rows x 128 bytes) and the weight
+// stage (128 rows x 64 or 128 bytes) are staged in LDS, rows padded to 144 bytes (the 16 lanes
+// of a 16-byte read hit 16 distinct bank groups), double-buffered: the next group's loads are
+// in flight in registers while the current group is multiplied.
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "atom_internal.h"
+
+namespace atom {
+namespace {
+
+typedef int32_t v4i __attribute__((ext_vector_type(4)));
+typedef int32_t v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 128;                 // output tile rows and columns
+constexpr int kThreads = 256;              // 4 waves
+constexpr int kLdsRow = 144;               // staged row: 128 bytes + 16 padding
+constexpr uint32_t kNibbles = 0x0F0F0F0Fu;
+constexpr int32_t kMinus8 = (int32_t)0xF8F8F8F8u;   // four int8 -8
+
+__device__ __forceinline__ v16i mma_i8(v4i w, v4i x, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(w, x, c, 0, 0, 0);
+}
+
+// Compile-time selector of the weight group kind (INT4 nibbles or the INT8 outlier group).
+template <bool B>
+struct WeightKind {
+  static constexpr bool value = B;
+};
+using Int4W = WeightKind<false>;
+using Int8W = WeightKind<true>;
+
+// 16 biased INT4 codes (two words of nibbles) -> int8 operand of the codes + 8
+__device__ __forceinline__ v4i unpack_nibbles(uint2 w) {
+  return v4i{(int)(w.x & kNibbles), (int)((w.x >> 4) & kNibbles), (int)(w.y & kNibbles),
+             (int)((w.y >> 4) & kNibbles)};
+}
+
+template <bool kAcc>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a8_kernel(
+    const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx, const uint8_t* __restrict__ Wq,
+    const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t la[2][kTile * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint8_t lb[2][kTile * kLdsRow];
+  __shared__ __attribute__((aligned(16))) h4 ls[2][2 * kTile];        // sx of the tile rows, then sw
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int tiles_m = (M + kTile - 1) / kTile;
+  const int m0 = (blockIdx.x % tiles_m) * kTile, n0 = (blockIdx.x / tiles_m) * kTile;
+  const int G = K / ATOM_GROUP;
+  const int klo = K - ATOM_OUTLIERS;
+  const size_t rbw = (size_t)klo / 2 + ATOM_OUTLIERS;      // weight row bytes
+
+  // Stage copy: thread tid moves chunks q = tid + 256 i (16 bytes each); activation chunk q is
+  // row q / 8, bytes 16 (q % 8) of the group; weight chunk q of an INT4 group is row q / 4,
+  // bytes 16 (q % 4) (two chunks per thread), of the INT8 group row q / 8, bytes 16 (q % 8)
+  // (four).  Rows past M / N repeat the last valid row (their results are never stored).
+  struct Stage {
+    uint4 a0, a1, a2, a3, w0, w1, w2, w3;
+    uint16_t s;
+  };
+  auto xload = [&](int g, int i) {
+    const int q = tid + kThreads * i;
+    return *reinterpret_cast<const uint4*>(Xq + (size_t)min(m0 + (q >> 3), M - 1) * K + (size_t)g * ATOM_GROUP +
+                                           16 * (q & 7));
+  };
+  auto wload4 = [&](int g, int i) {   // INT4 group, chunks 0..511
+    const int q = tid + kThreads * i;
+    return *reinterpret_cast<const uint4*>(Wq + (size_t)min(n0 + (q >> 2), N - 1) * rbw + (size_t)g * 64 + 16 * (q & 3));
+  };
+  auto wload8 = [&](int i) {          // INT8 group, chunks 0..1023
+    const int q = tid + kThreads * i;
+    return *reinterpret_cast<const uint4*>(Wq + (size_t)min(n0 + (q >> 3), N - 1) * rbw + klo / 2 + 16 * (q & 7));
+  };
+  auto load_stage = [&](auto int8w_tag, int g) {
+    constexpr bool kInt8W = decltype(int8w_tag)::value;
+    Stage st;
+    st.a0 = xload(g, 0);
+    st.a1 = xload(g, 1);
+    st.a2 = xload(g, 2);
+    st.a3 = xload(g, 3);
+    if (kInt8W) {
+      st.w0 = wload8(0);
+      st.w1 = wload8(1);
+      st.w2 = wload8(2);
+      st.w3 = wload8(3);
+    } else {
+      st.w0 = wload4(g, 0);
+      st.w1 = wload4(g, 1);
+      st.w2 = st.w3 = uint4{0, 0, 0, 0};
+    }
+    st.s = 0;
+    if (!kAcc)
+      st.s = tid < kTile ? sx[(size_t)g * M + min(m0 + tid, M - 1)] : sw[(size_t)g * N + min(n0 + tid - kTile, N - 1)];
+    return st;
+  };
+  auto lds_a = [&](int buf, int i) -> uint4* {
+    const int q = tid + kThreads * i;
+    return reinterpret_cast<uint4*>(&la[buf][(q >> 3) * kLdsRow + 16 * (q & 7)]);
+  };
+  auto lds_w4 = [&](int buf, int i) -> uint4* {
+    const int q = tid + kThreads * i;
+    return reinterpret_cast<uint4*>(&lb[buf][(q >> 2) * kLdsRow + 16 * (q & 3)]);
+  };
+  auto lds_w8 = [&](int buf, int i) -> uint4* {
+    const int q = tid + kThreads * i;
+    return reinterpret_cast<uint4*>(&lb[buf][(q >> 3) * kLdsRow + 16 * (q & 7)]);
+  };
+  auto store_stage = [&](auto int8w_tag, const Stage& st, int buf) {
+    constexpr bool kInt8W = decltype(int8w_tag)::value;
+    *lds_a(buf, 0) = st.a0;
+    *lds_a(buf, 1) = st.a1;
+    *lds_a(buf, 2) = st.a2;
+    *lds_a(buf, 3) = st.a3;
+    if (kInt8W) {
+      *lds_w8(buf, 0) = st.w0;
+      *lds_w8(buf, 1) = st.w1;
+      *lds_w8(buf, 2) = st.w2;
+      *lds_w8(buf, 3) = st.w3;
+    } else {
+      *lds_w4(buf, 0) = st.w0;
+      *lds_w4(buf, 1) = st.w1;
+    }
+    if (!kAcc) ls[buf][tid] = h4{__builtin_bit_cast(_Float16, st.s), (_Float16)0, (_Float16)0, (_Float16)0};
+  };
+
+  v16f yacc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) yacc[i][j][r] = 0.0f;
+
+  // Group g from LDS buffer buf into the Y accumulators (or, kAcc, to acc_out).
+  auto compute = [&](auto int8w_tag, int g, int buf) {
+    constexpr bool kInt8W = decltype(int8w_tag)::value;
+    h4 sa[2], sb[2];
+    if (!kAcc) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) sa[i] = ls[buf][wm * 64 + i * 32 + l32];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sb[j] = ls[buf][kTile + wn * 64 + j * 32 + l32];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_sched_barrier(0);   // one tile row's operands live at a time
+      const uint8_t* arow = &la[buf][(wm * 64 + i * 32 + l32) * kLdsRow + 16 * kh];
+      v4i a[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const v4i*>(arow + 32 * t);
+      v16i corr = {};
+      if (!kInt8W) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) corr = mma_i8(v4i{kMinus8, kMinus8, kMinus8, kMinus8}, a[t], corr);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        __builtin_amdgcn_sched_barrier(0);   // one output tile's sums and scale product live at a time
+        const uint8_t* brow = &lb[buf][(wn * 64 + j * 32 + l32) * kLdsRow];
+        v16i acc = corr;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v4i b;
+          if (kInt8W)
+            b = *reinterpret_cast<const v4i*>(brow + 32 * t + 16 * kh);
+          else
+            b = unpack_nibbles(*reinterpret_cast<const uint2*>(brow + 16 * t + 8 * kh));
+          acc = mma_i8(b, a[t], acc);
+        }
+        if (kAcc) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm * 64 + i * 32 + l32;
+            const int n = n0 + wn * 64 + j * 32 + (r >> 2) * 8 + kh * 4 + (r & 3);
+            if (m < M && n < N) acc_out[((size_t)g * M + m) * N + n] = acc[r];
+          }
+        } else {
+          const v16f sp = __builtin_amdgcn_mfma_f32_32x32x8f16(sb[j], sa[i], v16f{}, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) yacc[i][j][r] = __builtin_fmaf((float)acc[r], sp[r], yacc[i][j][r]);
+        }
+      }
+    }
+  };
+
+  // INT4 groups 0 .. G-2, the next group's loads in flight during each; then the INT8 group.
+  store_stage(Int4W{}, load_stage(Int4W{}, 0), 0);
+  __syncthreads();
+  for (int g = 0; g < G - 2; ++g) {
+    const Stage next = load_stage(Int4W{}, g + 1);
+    compute(Int4W{}, g, g & 1);
+    store_stage(Int4W{}, next, (g + 1) & 1);
+    __syncthreads();
+  }
+  {
+    const int g = G - 2;
+    const Stage next = load_stage(Int8W{}, G - 1);
+    compute(Int4W{}, g, g & 1);
+    store_stage(Int8W{}, next, (g + 1) & 1);
+    __syncthreads();
+  }
+  compute(Int8W{}, G - 1, (G - 1) & 1);
+
+  if (kAcc) return;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + wm * 64 + i * 32 + l32;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 64 + j * 32 + q * 8 + kh * 4;
+        const uint16_t o[4] = {__half_as_ushort(__float2half_rn(0.5f * yacc[i][j][4 * q])),
+                               __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][4 * q + 1])),
+                               __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][4 * q + 2])),
+                               __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][4 * q + 3]))};
+        if (m >= M) continue;
+        uint16_t* dst = Y + (size_t)m * N + n;
+        if (n + 4 <= N && (N & 3) == 0) {
+          *reinterpret_cast<ushort4*>(dst) = ushort4{o[0], o[1], o[2], o[3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) dst[e] = o[e];
+        }
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_w4a8(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M,
+                            int N, int K, uint16_t* Y, int32_t* acc, hipStream_t stream) {
+  const dim3 grid(((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile));
+  if (acc)
+    hipLaunchKernelGGL(gemm_w4a8_kernel<true>, grid, dim3(kThreads), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, acc);
+  else
+    hipLaunchKernelGGL(gemm_w4a8_kernel<false>, grid, dim3(kThreads), 0, stream, Xq, sx, Wq, sw, M, N, K, Y,
+                       (int32_t*)nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace atom

@@ -122,7 +122,7 @@ __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, ui
 // row (item / split = row, item % split = pass), used when there are fewer rows than resident
 // workgroups, so that a short batch still spreads over the chip (each item stages the whole
 // row, which an arbitrary reorder needs; the repeated row reads hit in L2).
-template <int CHUNKS, int PASSES>
+template <int CHUNKS, int PASSES, int FMT>
 __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* __restrict__ X,
                                                                 const int32_t* __restrict__ perm, int rows, int K,
                                                                 int split, uint8_t* __restrict__ Q,
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
   const int QP = staged_stride(K);
   const int G = K / ATOM_GROUP;
   const int klo = K - ATOM_OUTLIERS;
-  const size_t rb = (size_t)(klo / 2 + ATOM_OUTLIERS);
+  const size_t rb = FMT == kRowA8 ? (size_t)K : (size_t)(klo / 2 + ATOM_OUTLIERS);
   const int nchunks = K / 8;                         // 16-byte chunks per row
   const unsigned kmax = (unsigned)(K - 1);
   constexpr int kPassElems = kThreads * kPerThread;  // 4096
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
   // Quantize the 16 reordered elements at position c (gather offsets off) of the LDS row.
   auto quantize16 = [&](int c, const int (&off)[kPerThread], uint8_t* qrow, int row) {
     const int g = c / ATOM_GROUP;
-    const bool tail = g == G - 1;
+    const bool tail = FMT == kRowA8 || g == G - 1;     // INT8 codes
     // The elements stay fp16: the absmax is taken in fp16 (exact), and each fp32 step that
     // reads x takes it as a mixed-precision fma operand, so no element is converted.
     _Float16 x[kPerThread];
@@ -202,7 +202,17 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
     float v[kPerThread];
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) v[i] = code_value(x[i], s, r, qmax);
-    if (!tail) {
+    if (!tail && FMT == kRowW4A8) {
+      // offset-binary nibbles: adding 1.5 * 2^23 + 8 leaves code + 8 (1 .. 15) in the low
+      // byte; block k (codes 8k .. 8k+7) is the word whose byte j holds codes 8k+j and 8k+j+4
+      uint32_t bb[kPerThread];
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) bb[i] = __float_as_uint(v[i] + (kRound + 8.0f));
+      uint2 w;
+      w.x = pack4(bb[0], bb[1], bb[2], bb[3]) | (pack4(bb[4], bb[5], bb[6], bb[7]) << 4);
+      w.y = pack4(bb[8], bb[9], bb[10], bb[11]) | (pack4(bb[12], bb[13], bb[14], bb[15]) << 4);
+      *reinterpret_cast<uint2*>(qrow + c / 2) = w;
+    } else if (!tail) {
       // INT4 unit: the integer codes as fp16, then one conversion to fp6 e2m3 with scale 8
       // (code / 8, exact on the subnormal grid) that packs field i at bits 6i of T0:T1:T2; T2
       // is then folded into the exponent bits of T0 and T1
@@ -230,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
       w.y = pack4(b[4], b[5], b[6], b[7]);
       w.z = pack4(b[8], b[9], b[10], b[11]);
       w.w = pack4(b[12], b[13], b[14], b[15]);
-      *reinterpret_cast<u32x4*>(qrow + klo / 2 + (c - klo)) = w;
+      *reinterpret_cast<u32x4*>(qrow + (FMT == kRowA8 ? c : klo / 2 + (c - klo))) = w;
     }
     if ((threadIdx.x & (kLanesPerGroup - 1)) == 0) S[(size_t)g * rows + row] = __half_as_ushort(s16);
   };
@@ -299,7 +309,7 @@ struct Residency {
   int per_cu, cus;
 };
 
-template <int CHUNKS, int PASSES>
+template <int CHUNKS, int PASSES, int FMT>
 Residency query_residency() {
   Residency r{2, 256};                               // fallbacks if a query fails
   int dev = 0, n = 0, b = 0;
@@ -307,19 +317,19 @@ Residency query_residency() {
       n > 0)
     r.cus = n;
   const size_t lds_max = (size_t)staged_stride(CHUNKS * 8 * kThreads) * 8 * sizeof(uint32_t);   // largest row of this range
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, row_quantize_kernel<CHUNKS, PASSES>, kThreads, lds_max) ==
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, row_quantize_kernel<CHUNKS, PASSES, FMT>, kThreads, lds_max) ==
           hipSuccess && b > 0)
     r.per_cu = b;
   return r;
 }
 
-template <int CHUNKS, int PASSES>
+template <int CHUNKS, int PASSES, int FMT>
 hipError_t launch_rq(const uint16_t* X, const int32_t* perm, int rows, int K, uint8_t* Q, uint16_t* S,
                      hipStream_t stream) {
   const size_t lds = (size_t)staged_stride(K) * 8 * sizeof(uint32_t);
   // queried once per process and instantiation (the initialisation of a function-local static
   // is thread-safe), on the device current at the first call
-  static const Residency res = query_residency<CHUNKS, PASSES>();
+  static const Residency res = query_residency<CHUNKS, PASSES, FMT>();
   const int per_cu = res.per_cu, cus = res.cus;
   const int lim = per_cu * cus;
   // passes of a row as separate items when the rows alone leave resident slots empty
@@ -327,20 +337,32 @@ hipError_t launch_rq(const uint16_t* X, const int32_t* perm, int rows, int K, ui
   const int split = (PASSES > 1 && rows < lim) ? passes : 1;
   const long long items = (long long)rows * split;
   const int grid = items < lim ? (int)items : lim;   // persistent: one wave of workgroups
-  hipLaunchKernelGGL((row_quantize_kernel<CHUNKS, PASSES>), dim3(grid), dim3(kThreads), lds, stream, X, perm, rows,
+  hipLaunchKernelGGL((row_quantize_kernel<CHUNKS, PASSES, FMT>), dim3(grid), dim3(kThreads), lds, stream, X, perm, rows,
                      K, split, Q, S);
   return hipGetLastError();
+}
+
+
+template <int FMT>
+hipError_t launch_rq_fmt(const uint16_t* X, const int32_t* perm, int rows, int K, uint8_t* Q, uint16_t* S,
+                         hipStream_t stream) {
+  if (K <= 4096) return launch_rq<2, 1, FMT>(X, perm, rows, K, Q, S, stream);
+  if (K <= 8192) return launch_rq<4, 2, FMT>(X, perm, rows, K, Q, S, stream);
+  if (K <= 12288) return launch_rq<6, 3, FMT>(X, perm, rows, K, Q, S, stream);
+  if (K <= 16384) return launch_rq<8, 4, FMT>(X, perm, rows, K, Q, S, stream);
+  return launch_rq<ATOM_MAX_K / 8 / kThreads, 0, FMT>(X, perm, rows, K, Q, S, stream);
 }
 
 }  // namespace
 
 hipError_t launch_row_quantize(const uint16_t* X, const int32_t* perm, int rows, int K, uint8_t* Q, uint16_t* S,
-                               hipStream_t stream) {
-  if (K <= 4096) return launch_rq<2, 1>(X, perm, rows, K, Q, S, stream);
-  if (K <= 8192) return launch_rq<4, 2>(X, perm, rows, K, Q, S, stream);
-  if (K <= 12288) return launch_rq<6, 3>(X, perm, rows, K, Q, S, stream);
-  if (K <= 16384) return launch_rq<8, 4>(X, perm, rows, K, Q, S, stream);
-  return launch_rq<ATOM_MAX_K / 8 / kThreads, 0>(X, perm, rows, K, Q, S, stream);
+                               RowFormat fmt, hipStream_t stream) {
+  switch (fmt) {
+    case kRowW4A4: return launch_rq_fmt<kRowW4A4>(X, perm, rows, K, Q, S, stream);
+    case kRowA8: return launch_rq_fmt<kRowA8>(X, perm, rows, K, Q, S, stream);
+    case kRowW4A8: return launch_rq_fmt<kRowW4A8>(X, perm, rows, K, Q, S, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace atom

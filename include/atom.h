@@ -158,6 +158,33 @@ int atom_gemm_ws(const void *Xq, const void *sx, const void *Wq, const void *sw,
 int atom_gemm_group_acc(const void *Xq, const void *Wq, int32_t M, int32_t N, int32_t K,
                         int32_t *acc, void *stream);
 
+/*
+ * W4A8 variant (a next step beside the W4A4 path; the pages point to INT8 activations only as
+ * the precision another method's kernels target).  Activations get INT8 codes in every group
+ * (the rule of atom_quantize_act with qmax = 127 for every group); weights keep the W4 rule of
+ * atom_pack_weights but a layout the int8 matrix cores unpack cheaply.  The product and the
+ * output are defined as for atom_gemm.
+ *
+ * atom_quantize_act_a8: X const fp16 [M, K], perm const int32 [K] -> Xq uint8 [M, K] (one
+ *   two's-complement byte per code, reordered order), sx fp16 [G, M].
+ * atom_pack_weights_w4a8: W const fp16 [N, K], perm -> Wq uint8 [N, RB], sw fp16 [G, N].  Codes
+ *   and scales equal atom_pack_weights'; the first (K-128)/2 bytes hold the INT4 codes in blocks
+ *   of 8 consecutive codes c_0..c_7 as 4 bytes, byte j = (c_j + 8) | (c_{j+4} + 8) << 4
+ *   (offset binary); the last 128 bytes hold the INT8 outlier codes, two's complement.
+ * atom_gemm_w4a8: Xq [M, K] from atom_quantize_act_a8, Wq [N, RB] from atom_pack_weights_w4a8,
+ *   scales as above -> Y fp16 [M, N] = fp16_rne(sum_g acc_g * sx[g,m] * sw[g,n]), fp32 scaling.
+ * atom_gemm_w4a8_group_acc: acc int32 [G, M, N] of the same operands (verification aid).
+ * Shapes, alignment, overlap and error rules as for the W4A4 calls.
+ */
+int atom_quantize_act_a8(const void *X, const int32_t *perm, int32_t M, int32_t K, void *Xq, void *sx,
+                         void *stream);
+int atom_pack_weights_w4a8(const void *W, const int32_t *perm, int32_t N, int32_t K, void *Wq, void *sw,
+                           void *stream);
+int atom_gemm_w4a8(const void *Xq, const void *sx, const void *Wq, const void *sw, int32_t M, int32_t N,
+                   int32_t K, void *Y, void *stream);
+int atom_gemm_w4a8_group_acc(const void *Xq, const void *Wq, int32_t M, int32_t N, int32_t K, int32_t *acc,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif

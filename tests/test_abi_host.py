@@ -33,7 +33,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 15
     assert sorted(bq.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -114,6 +114,30 @@ def test_gemm_validation(lib):
     assert g(A, B, C, D, 4, 4, 256, D, S) == E_OVERLAP          # Y on sw
     ga = lib.atom_gemm_group_acc
     assert ga(A, None, 4, 4, 256, E, S) == E_NULL
+    assert ga(A, C, 4, 4, 200, E, S) == E_SHAPE
+    assert ga(A, C, 4, 4, 256, E + 4, S) == E_ALIGN
+    assert ga(A, C, 4, 4, 256, C + 64, S) == E_OVERLAP
+
+
+def test_w4a8_validation(lib):
+    qa = lib.atom_quantize_act_a8
+    assert qa(None, B, 4, 256, C, D, S) == E_NULL
+    assert qa(A, B, 4, 300, C, D, S) == E_SHAPE
+    assert qa(A, B, 4, 256, C + 2, D, S) == E_ALIGN
+    # the A8 row is K bytes: Q (4 x 256 bytes) reaches C + 1024
+    assert qa(A, B, 4, 256, C, C + 1008, S) == E_OVERLAP
+    pw = lib.atom_pack_weights_w4a8
+    assert pw(A, None, 4, 256, C, D, S) == E_NULL
+    assert pw(A, B, 4, 128, C, D, S) == E_SHAPE
+    assert pw(A, B, 4, 256, C, C + 512, S) == E_OVERLAP      # sw inside Wq (4 x 192 bytes)
+    g = lib.atom_gemm_w4a8
+    assert g(None, B, C, D, 4, 4, 256, E, S) == E_NULL
+    assert g(A, None, C, D, 4, 4, 256, E, S) == E_NULL
+    assert g(A, B, C, D, 4, 0, 256, E, S) == E_SHAPE
+    assert g(A, B, C, D + 2, 4, 4, 256, E, S) == E_ALIGN
+    assert g(A, B, C, D, 4, 4, 256, A + 512, S) == E_OVERLAP    # Y inside Xq (4 x 256 bytes)
+    ga = lib.atom_gemm_w4a8_group_acc
+    assert ga(A, C, 4, 4, 256, None, S) == E_NULL
     assert ga(A, C, 4, 4, 200, E, S) == E_SHAPE
     assert ga(A, C, 4, 4, 256, E + 4, S) == E_ALIGN
     assert ga(A, C, 4, 4, 256, C + 64, S) == E_OVERLAP
