@@ -44,6 +44,8 @@ WORKLOAD_SETS = {
     "A": ["A"], "B": ["B"], "C": ["C"], "D": ["D"],
     # 16 tokens through the same weights: the few-rows GEMM, bound by reading the packed weights
     "decode": ["dA", "dB", "dC"],
+    # the W4A8 variant (INT8 activations in every group) on the same Llama-7B shapes
+    "w4a8": ["A", "B", "C"],
     "Dq": [],              # activation quantize alone on 8192 x 8192 fp16 (128 outlier channels x30)
 }
 
@@ -98,9 +100,10 @@ class _nullctx:
         return False
 
 
-def cpu_baseline(shapes, budget_rows):
+def cpu_baseline(shapes, budget_rows, a8=False):
     """Time the CPU oracle (quantize + dequantise-then-fp64-matmul) on a row sample of every
-    shape; weights are packed by the oracle beforehand, like the GPU path."""
+    shape; weights are packed by the oracle beforehand, like the GPU path.  a8: INT8 codes in
+    every activation group (the W4A8 variant)."""
     import synth
     from oracle import atom_oracle as O
     try:
@@ -121,7 +124,7 @@ def cpu_baseline(shapes, budget_rows):
             qw, sw = O.quantize_rows(wt, perm)
             xs = np.ascontiguousarray(x[:rows])
             t0 = time.perf_counter()
-            qx, sx = O.quantize_rows(xs, perm)
+            qx, sx = O.quantize_rows(xs, perm, all_int8=a8)
             y = O.to_fp16(O.gemm_ref(qx, sx, qw, sw))
             dt = time.perf_counter() - t0
             assert y.shape == (rows, w.N)
@@ -225,6 +228,7 @@ def main():
         return quant_only(args, torch, bq, synth, dev, R)
 
     # ---------------------------------------------------------------- offline: inputs, perm, weight pack
+    w4a8 = args.workload == "w4a8"
     sets = []
     for key in keys:
         w = synth.get(key)
@@ -232,18 +236,19 @@ def main():
         X0 = torch.from_numpy(x).to(dev)
         W0 = torch.from_numpy(wt).to(dev)
         perm = bq.atom_select_outliers(bq.atom_channel_stat(X0))
-        Wq0, sw0 = bq.atom_pack_weights(W0, perm)
+        Wq0, sw0 = (bq.atom_pack_weights_w4a8 if w4a8 else bq.atom_pack_weights)(W0, perm)
         del W0
         copies = []
         for r in range(R):
             # distinct resident copies; activations get a tiny per-copy change so codes differ
             Xr = X0.clone() if r == 0 else (X0 * (1.0 + 1e-3 * r)).to(torch.float16)
             copies.append(dict(X=Xr, Wq=Wq0.clone(), sw=sw0.clone(),
-                               Xq=torch.empty((w.M, bq.atom_row_bytes(w.K)), dtype=torch.uint8, device=dev),
+                               Xq=torch.empty((w.M, w.K if w4a8 else bq.atom_row_bytes(w.K)), dtype=torch.uint8,
+                                              device=dev),
                                sx=torch.empty((w.K // 128, w.M), dtype=torch.float16, device=dev),
                                Y=torch.empty((w.M, w.N), dtype=torch.float16, device=dev)))
         # split-K scratch for shapes with few output tiles (allocated once, outside the timed region)
-        need = bq.atom_gemm_workspace_bytes(w.M, w.N, w.K)
+        need = 0 if w4a8 else bq.atom_gemm_workspace_bytes(w.M, w.N, w.K)
         ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
         sets.append(dict(key=key, w=w, perm=perm, copies=copies, ws=ws))
         log(f"[setup] {key} {w.name} ready ({R} copies)")
@@ -257,10 +262,16 @@ def main():
             w = s["w"]
             if evs is not None:
                 evs[si][0].record(stream)
-            bq.atom_quantize_act(c["X"], s["perm"], Xq=c["Xq"], sx=c["sx"], stream=stream)
+            if w4a8:
+                bq.atom_quantize_act_a8(c["X"], s["perm"], Xq=c["Xq"], sx=c["sx"], stream=stream)
+            else:
+                bq.atom_quantize_act(c["X"], s["perm"], Xq=c["Xq"], sx=c["sx"], stream=stream)
             if evs is not None:
                 evs[si][1].record(stream)
-            bq.atom_gemm_ws(c["Xq"], c["sx"], c["Wq"], c["sw"], w.K, s["ws"], Y=c["Y"], stream=stream)
+            if w4a8:
+                bq.atom_gemm_w4a8(c["Xq"], c["sx"], c["Wq"], c["sw"], w.K, Y=c["Y"], stream=stream)
+            else:
+                bq.atom_gemm_ws(c["Xq"], c["sx"], c["Wq"], c["sw"], w.K, s["ws"], Y=c["Y"], stream=stream)
             if evs is not None:
                 evs[si][2].record(stream)
 
@@ -307,7 +318,7 @@ def main():
     for s in sets:
         w = s["w"]
         p = per[w.key]
-        qb = quant_bytes(w.M, w.K)
+        qb = quant_bytes(w.M, w.K) + (w.M * (w.K - (w.K - 128) // 2 - 128) if w4a8 else 0)   # A8 rows are K bytes
         shapes[w.key] = {
             "name": w.name, "M": w.M, "K": w.K, "N": w.N,
             "quant_us": round(p["quant_us"], 2), "gemm_us": round(p["gemm_us"], 2),
@@ -329,7 +340,8 @@ def main():
             traffic = float(np.mean(vals))
 
     line = {
-        "metric": "effective W4A4 TOPS (quant+GEMM) at Llama-7B shapes; % of INT8 MFMA peak",
+        "metric": ("effective W4A8 TOPS (quant+GEMM) at Llama-7B shapes; % of INT8 MFMA peak" if w4a8 else
+                   "effective W4A4 TOPS (quant+GEMM) at Llama-7B shapes; % of INT8 MFMA peak"),
         "value": round(value, 2),
         "unit": "TOP/s",
         "n_gpus": 1,
@@ -340,15 +352,23 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "frac_int8_peak": round(value / INT8_PEAK_TOPS, 4),
-        "dtype": "int4 via fp6e2m3 mfma + int8",
+        "dtype": "int8 x int4 via int8 mfma" if w4a8 else "int4 via fp6e2m3 mfma + int8",
         "data": "synthetic",
         "config": {
-            "workload": "llama7b_linear_" + "_".join(s["w"].name for s in sets) if len(sets) > 1 else sets[0]["w"].name,
+            "workload": ("w4a8_" if w4a8 else "") + ("llama7b_linear_" + "_".join(s["w"].name for s in sets)
+                                                      if len(sets) > 1 else sets[0]["w"].name),
             "shapes_MxKxN": [f'{s["w"].M}x{s["w"].K}x{s["w"].N}' for s in sets],
-            "group": 128, "outlier_channels": 128, "weights": "pre-packed INT4 + INT8 outlier group",
+            "group": 128, "outlier_channels": 128,
+            "weights": "pre-packed INT4 + INT8 outlier group" + (" (offset-binary nibbles)" if w4a8 else ""),
+            "activations": "INT8 in every group" if w4a8 else "INT4 + INT8 outlier group",
             "rotating_input_copies": R,
         },
         "roofline": {
+            # every W4A8 group runs on the int8 matrix cores
+            "kernel": "gemm_w4a8_kernel", "bound": "mfma", "achieved": round(gemm_tops, 1),
+            "peak": round(INT8_PEAK_TOPS, 1), "unit": "TOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+            "traffic": None, "ops_per_launch": gemm_ops / len(sets), "avg_launch_us": round(gemm_us / len(sets), 3),
+        } if w4a8 else {
             "kernel": "gemm_w4a4_kernel", "bound": "mfma", "achieved": round(gemm_tops, 1),
             "peak": round(FP6_PEAK_TOPS, 1), "unit": "TOP/s", "frac": round(gemm_tops / FP6_PEAK_TOPS, 4),
             "traffic": traffic, "ops_per_launch": gemm_ops / len(sets),
@@ -364,7 +384,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[cpu] timing the oracle on a row sample")
-        line["cpu_baseline"] = cpu_baseline(keys, args.cpu_rows)
+        line["cpu_baseline"] = cpu_baseline(keys, args.cpu_rows, a8=w4a8)
     print(json.dumps(line), flush=True)
 
 
