@@ -192,7 +192,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        __builtin_amdgcn_sched_barrier(0);   // one output tile's sums and scale product live at a time
         const uint8_t* brow = &lb[buf][(wn * 64 + j * 32 + l32) * kLdsRow];
         v16i acc = corr;
 #pragma unroll
