@@ -248,7 +248,7 @@ def main():
                                sx=torch.empty((w.K // 128, w.M), dtype=torch.float16, device=dev),
                                Y=torch.empty((w.M, w.N), dtype=torch.float16, device=dev)))
         # split-K scratch for shapes with few output tiles (allocated once, outside the timed region)
-        need = 0 if w4a8 else bq.atom_gemm_workspace_bytes(w.M, w.N, w.K)
+        need = (bq.atom_gemm_w4a8_workspace_bytes if w4a8 else bq.atom_gemm_workspace_bytes)(w.M, w.N, w.K)
         ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
         sets.append(dict(key=key, w=w, perm=perm, copies=copies, ws=ws))
         log(f"[setup] {key} {w.name} ready ({R} copies)")
@@ -269,7 +269,7 @@ def main():
             if evs is not None:
                 evs[si][1].record(stream)
             if w4a8:
-                bq.atom_gemm_w4a8(c["Xq"], c["sx"], c["Wq"], c["sw"], w.K, Y=c["Y"], stream=stream)
+                bq.atom_gemm_w4a8_ws(c["Xq"], c["sx"], c["Wq"], c["sw"], w.K, s["ws"], Y=c["Y"], stream=stream)
             else:
                 bq.atom_gemm_ws(c["Xq"], c["sx"], c["Wq"], c["sw"], w.K, s["ws"], Y=c["Y"], stream=stream)
             if evs is not None:

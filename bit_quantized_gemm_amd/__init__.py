@@ -27,7 +27,7 @@ __all__ = [
     "atom_row_bytes", "atom_num_groups", "atom_strerror", "atom_channel_stat", "atom_select_outliers",
     "atom_pack_weights", "atom_quantize_act", "atom_gemm", "atom_gemm_workspace_bytes", "atom_gemm_ws",
     "atom_gemm_group_acc", "linear", "atom_quantize_act_a8", "atom_pack_weights_w4a8", "atom_gemm_w4a8",
-    "atom_gemm_w4a8_group_acc",
+    "atom_gemm_w4a8_group_acc", "atom_gemm_w4a8_workspace_bytes", "atom_gemm_w4a8_ws",
 ]
 
 GROUP = 128
@@ -39,7 +39,7 @@ EXPORTS = (
     "atom_row_bytes", "atom_num_groups", "atom_strerror", "atom_channel_stat", "atom_select_outliers",
     "atom_pack_weights", "atom_quantize_act", "atom_gemm", "atom_gemm_workspace_bytes", "atom_gemm_ws",
     "atom_gemm_group_acc", "atom_quantize_act_a8", "atom_pack_weights_w4a8", "atom_gemm_w4a8",
-    "atom_gemm_w4a8_group_acc",
+    "atom_gemm_w4a8_group_acc", "atom_gemm_w4a8_workspace_bytes", "atom_gemm_w4a8_ws",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -80,6 +80,8 @@ def load_library():
         "atom_pack_weights_w4a8": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp]),
         "atom_gemm_w4a8": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp]),
         "atom_gemm_w4a8_group_acc": (ctypes.c_int, [vp, vp, i32, i32, i32, vp, vp]),
+        "atom_gemm_w4a8_workspace_bytes": (i64, [i32, i32, i32]),
+        "atom_gemm_w4a8_ws": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp, i64, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -305,3 +307,28 @@ def atom_gemm_w4a8_group_acc(Xq, Wq, K, acc=None, stream=None):
                                                  _dev(acc, "acc", torch.int32), _stream(stream, Xq.device))
     _check(st, "atom_gemm_w4a8_group_acc")
     return acc
+
+
+def atom_gemm_w4a8_workspace_bytes(M: int, N: int, K: int) -> int:
+    r = load_library().atom_gemm_w4a8_workspace_bytes(M, N, K)
+    if r < 0:
+        raise AtomError(f"atom_gemm_w4a8_workspace_bytes: {atom_strerror(-r)}")
+    return r
+
+
+def atom_gemm_w4a8_ws(Xq, sx, Wq, sw, K, workspace, Y=None, stream=None):
+    """atom_gemm_w4a8 with a caller-allocated split-K workspace (uint8 tensor, or None)."""
+    torch = _torch()
+    M = Xq.shape[0]
+    N = Wq.shape[0]
+    if Y is None:
+        Y = _empty((M, N), torch.float16, Xq)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace", torch.uint8)
+        ws_bytes = workspace.numel()
+    st = load_library().atom_gemm_w4a8_ws(_dev(Xq, "Xq", torch.uint8), _dev(sx, "sx", torch.float16),
+                                          _dev(Wq, "Wq", torch.uint8), _dev(sw, "sw", torch.float16), M, N, K,
+                                          _dev(Y, "Y", torch.float16), ws_ptr, ws_bytes, _stream(stream, Xq.device))
+    _check(st, "atom_gemm_w4a8_ws")
+    return Y

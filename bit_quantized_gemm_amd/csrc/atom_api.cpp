@@ -186,7 +186,7 @@ int atom_pack_weights_w4a8(const void* W, const int32_t* perm, int32_t N, int32_
 }
 
 static int w4a8_common(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N,
-                       int32_t K, void* Y, int32_t* acc, void* stream) {
+                       int32_t K, void* Y, int32_t* acc, void* workspace, int64_t workspace_bytes, void* stream) {
   const bool want_acc = acc != nullptr;
   if (!Xq || !Wq || (want_acc ? false : (!sx || !sw || !Y))) return ATOM_E_NULL;
   if (!valid_gemm(M, N, K)) return ATOM_E_SHAPE;
@@ -199,26 +199,48 @@ static int w4a8_common(const void* Xq, const void* sx, const void* Wq, const voi
     const Range in[2] = {range_of(Xq, (uint64_t)M * K), range_of(Wq, (uint64_t)N * rbw)};
     const Range out[1] = {range_of(acc, G * M * N * 4)};
     if (int s = check_overlap(in, 2, out, 1)) return s;
-  } else {
-    const Range in[4] = {range_of(Xq, (uint64_t)M * K), range_of(sx, G * M * 2), range_of(Wq, (uint64_t)N * rbw),
-                         range_of(sw, G * N * 2)};
-    const Range out[1] = {range_of(Y, (uint64_t)M * N * 2)};
-    if (int s = check_overlap(in, 4, out, 1)) return s;
+    return hip_status(atom::launch_gemm_w4a8(static_cast<const uint8_t*>(Xq), nullptr,
+                                             static_cast<const uint8_t*>(Wq), nullptr, M, N, K, nullptr, acc,
+                                             nullptr, atom::GemmPlan{0, 0, 1, 0}, static_cast<hipStream_t>(stream)));
   }
+  atom::GemmPlan plan = atom::gemm_plan_tiled(M, N, K);
+  int64_t need = atom::gemm_workspace_bytes(plan);
+  if (need > 0 && (!workspace || workspace_bytes < need)) {   // too little scratch: unsplit
+    plan = atom::GemmPlan{((M + 127) / 128) * ((N + 127) / 128), 0, 1, 0};
+    need = 0;
+  }
+  const bool split = need > 0;
+  if (split && !aligned16(workspace)) return ATOM_E_ALIGN;
+  const Range in[4] = {range_of(Xq, (uint64_t)M * K), range_of(sx, G * M * 2), range_of(Wq, (uint64_t)N * rbw),
+                       range_of(sw, G * N * 2)};
+  const Range out[2] = {range_of(Y, (uint64_t)M * N * 2), range_of(workspace, split ? (uint64_t)need : 0)};
+  if (int s = check_overlap(in, 4, out, split ? 2 : 1)) return s;
   return hip_status(atom::launch_gemm_w4a8(static_cast<const uint8_t*>(Xq), static_cast<const uint16_t*>(sx),
                                            static_cast<const uint8_t*>(Wq), static_cast<const uint16_t*>(sw), M, N,
-                                           K, static_cast<uint16_t*>(Y), acc, static_cast<hipStream_t>(stream)));
+                                           K, static_cast<uint16_t*>(Y), nullptr,
+                                           split ? static_cast<float*>(workspace) : nullptr, plan,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int atom_gemm_w4a8(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N, int32_t K,
                    void* Y, void* stream) {
-  return w4a8_common(Xq, sx, Wq, sw, M, N, K, Y, nullptr, stream);
+  return w4a8_common(Xq, sx, Wq, sw, M, N, K, Y, nullptr, nullptr, 0, stream);
+}
+
+int64_t atom_gemm_w4a8_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (!valid_gemm(M, N, K)) return -(int64_t)ATOM_E_SHAPE;
+  return atom::gemm_workspace_bytes(atom::gemm_plan_tiled(M, N, K));
+}
+
+int atom_gemm_w4a8_ws(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N,
+                      int32_t K, void* Y, void* workspace, int64_t workspace_bytes, void* stream) {
+  return w4a8_common(Xq, sx, Wq, sw, M, N, K, Y, nullptr, workspace, workspace_bytes, stream);
 }
 
 int atom_gemm_w4a8_group_acc(const void* Xq, const void* Wq, int32_t M, int32_t N, int32_t K, int32_t* acc,
                              void* stream) {
   if (!acc) return ATOM_E_NULL;
-  return w4a8_common(Xq, nullptr, Wq, nullptr, M, N, K, nullptr, acc, stream);
+  return w4a8_common(Xq, nullptr, Wq, nullptr, M, N, K, nullptr, acc, nullptr, 0, stream);
 }
 
 }  // extern "C"

@@ -39,6 +39,24 @@ struct GemmPlan {
 // Few-rows kernel: at most kSmallMaxM token rows.
 constexpr int kSmallMaxM = 16;
 GemmPlan gemm_plan(int M, int N, int K);
+// The same plan for the 128 x 128 tiled kernels only (no few-rows branch).
+GemmPlan gemm_plan_tiled(int M, int N, int K);
+// Adds the fp32 partial tiles of a split plan (tile-major, piece p of split tile t at
+// part[(p * rem + t) * 128 * 128], row-major inside the tile, carrying the factor 2 of the scale
+// products) in piece order and writes Y.
+hipError_t launch_splitk_finish(const float* part, const GemmPlan& plan, int M, int N, uint16_t* Y,
+                                hipStream_t stream);
+
+// Output tile order of the tiled GEMM kernels: tiles are numbered in bands of kBandM tile rows,
+// M fastest inside a band, so a run of 64 consecutive tiles is an 8 x 8 block.  Returns the
+// tile's row and column index.
+constexpr int kBandM = 8;
+__host__ __device__ inline int2 tile_coords(int lin, int tiles_m, int tiles_n) {
+  const int band = lin / (kBandM * tiles_n), first_m = band * kBandM;
+  const int band_m = min(tiles_m - first_m, kBandM);     // tile rows in this band
+  const int in_band = lin - band * kBandM * tiles_n;
+  return int2{first_m + in_band % band_m, in_band / band_m};
+}
 // Scratch bytes the plan needs (0 when it writes Y directly).
 int64_t gemm_workspace_bytes(const GemmPlan& plan);
 // `part` holds gemm_workspace_bytes(plan) bytes of scratch when that is > 0, else unused.
@@ -51,7 +69,10 @@ hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, in
                                  hipStream_t stream);
 // W4A8 GEMM (gemm_w4a8.hip): Xq in kRowA8 rows, Wq in kRowW4A8 rows.  acc != nullptr: write
 // the per-group int32 accumulators [G, M, N] instead of Y.
+// plan: gemm_plan_tiled(M, N, K), or an unsplit plan; `part` holds gemm_workspace_bytes(plan)
+// bytes when the plan splits.
 hipError_t launch_gemm_w4a8(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M,
-                            int N, int K, uint16_t* Y, int32_t* acc, hipStream_t stream);
+                            int N, int K, uint16_t* Y, int32_t* acc, float* part, const GemmPlan& plan,
+                            hipStream_t stream);
 
 }  // namespace atom

@@ -60,7 +60,6 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 constexpr int kStageBytes = 64;          // bytes of one stage of a packed row
 constexpr int kLdsRow = 64;              // bytes of one staged (packed) row in LDS
 constexpr int kXcds = 8;                 // accelerator complex dies (each with its own L2)
-constexpr int kBandM = 8;                // tile rows per band of the tile order
 constexpr int kScaleE8M0 = 127 + 3;      // 2^3: the e2m3 subnormal q / 8 counts as q
 
 // fp6 operand (32 codes, six words) of the two packed units in words 4h .. 4h+3 of w: unit
@@ -136,15 +135,6 @@ struct Tile {
   static_assert(BM + BN == kThreads, "one scale per thread per stage");
   static_assert(BM == BN && kDma * kWaves * 16 == BM, "each wave copies whole 16-row slabs of A and B");
 };
-
-// Tile order: tiles are numbered in bands of kBandM tile rows, M fastest inside a band, so a
-// run of 64 consecutive tiles is an 8 x 8 block.  Returns the tile's row and column index.
-__device__ __forceinline__ int2 tile_coords(int lin, int tiles_m, int tiles_n) {
-  const int band = lin / (kBandM * tiles_n), first_m = band * kBandM;
-  const int band_m = min(tiles_m - first_m, kBandM);     // tile rows in this band
-  const int in_band = lin - band * kBandM * tiles_n;
-  return int2{first_m + in_band % band_m, in_band / band_m};
-}
 
 // Per-thread addressing of the stage copy, fixed for the whole K loop.  Wave w copies tile
 // rows [w * BM / W, (w + 1) * BM / W) of A and the same rows of B (W waves), 16 rows per
@@ -573,9 +563,13 @@ __global__ __launch_bounds__(256) void gemm_splitk_finish_kernel(const float* __
 }  // namespace
 
 GemmPlan gemm_plan(int M, int N, int K) {
+  if (M <= kSmallMaxM) return GemmPlan{0, 0, 1, 1};
+  return gemm_plan_tiled(M, N, K);
+}
+
+GemmPlan gemm_plan_tiled(int M, int N, int K) {
   const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   const int G = K / ATOM_GROUP;
-  if (M <= kSmallMaxM) return GemmPlan{0, 0, 1, 1};
   if (tiles >= kSplitMinTiles) return GemmPlan{tiles, 0, 1, 0};
   const int s = min(min((kSplitTargetBlocks + tiles - 1) / tiles, (G - 1) / kSplitMinGroups), kSplitMax);
   return s < 2 ? GemmPlan{tiles, 0, 1, 0} : GemmPlan{0, tiles, s, 0};
@@ -589,19 +583,25 @@ int64_t gemm_workspace_bytes(const GemmPlan& plan) {
 hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
                        int K, uint16_t* Y, float* part, const GemmPlan& plan, hipStream_t stream) {
   if (plan.small) return launch_gemm_small(Xq, sx, Wq, sw, M, N, K, Y, stream);
-  using Finish = void (*)(const float*, int, int, int, int, uint16_t*);
-  static constexpr Finish kFinish[kSplitMax + 1] = {
-      nullptr, nullptr, gemm_splitk_finish_kernel<2>, gemm_splitk_finish_kernel<3>, gemm_splitk_finish_kernel<4>,
-      gemm_splitk_finish_kernel<5>, gemm_splitk_finish_kernel<6>, gemm_splitk_finish_kernel<7>,
-      gemm_splitk_finish_kernel<8>};
   if (plan.rem > 0 && (plan.splits < 2 || plan.splits > kSplitMax)) return hipErrorInvalidValue;
   const int blocks = plan.full + plan.rem * plan.splits;
   hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, false>), dim3(blocks),
                      dim3(kWavesM * kWavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr,
                      plan.full, plan.rem, plan.splits, part);
-  if (plan.rem > 0)
-    hipLaunchKernelGGL(kFinish[plan.splits], dim3(kBM * kBN / 4 / 256, plan.rem), dim3(256), 0, stream, part,
-                       plan.full, plan.rem, M, N, Y);
+  if (plan.rem > 0) return launch_splitk_finish(part, plan, M, N, Y, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_finish(const float* part, const GemmPlan& plan, int M, int N, uint16_t* Y,
+                                hipStream_t stream) {
+  using Finish = void (*)(const float*, int, int, int, int, uint16_t*);
+  static constexpr Finish kFinish[kSplitMax + 1] = {
+      nullptr, nullptr, gemm_splitk_finish_kernel<2>, gemm_splitk_finish_kernel<3>, gemm_splitk_finish_kernel<4>,
+      gemm_splitk_finish_kernel<5>, gemm_splitk_finish_kernel<6>, gemm_splitk_finish_kernel<7>,
+      gemm_splitk_finish_kernel<8>};
+  if (plan.rem <= 0 || plan.splits < 2 || plan.splits > kSplitMax) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kFinish[plan.splits], dim3(kBM * kBN / 4 / 256, plan.rem), dim3(256), 0, stream, part,
+                     plan.full, plan.rem, M, N, Y);
   return hipGetLastError();
 }
 

@@ -28,7 +28,9 @@
 // per element and group; the factor 2 goes at the store.
 //
 // Work layout.  One workgroup of 4 waves per 128 x 128 output tile (2 x 2 waves of 64 x 64,
-// each 2 x 2 MFMA tiles).  Per group the activation stage (128 rows x 128 bytes) and the weight
+// each 2 x 2 MFMA tiles), tiles in the banded order of the W4A4 kernel; with caller scratch, a
+// grid of few tiles splits each tile's groups among pieces whose fp32 partial tiles the W4A4
+// split-K finalize adds.  Per group the activation stage (128 rows x 128 bytes) and the weight
 // stage (128 rows x 64 or 128 bytes) are staged in LDS, rows padded to 144 bytes (the 16 lanes
 // of a 16-byte read hit 16 distinct bank groups), double-buffered: the next group's loads are
 // in flight in registers while the current group is multiplied.
@@ -73,7 +75,8 @@ __device__ __forceinline__ v4i unpack_nibbles(uint2 w) {
 template <bool kAcc>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a8_kernel(
     const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx, const uint8_t* __restrict__ Wq,
-    const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out) {
+    const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out,
+    int rem, int splits, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint8_t la[2][kTile * kLdsRow];
   __shared__ __attribute__((aligned(16))) uint8_t lb[2][kTile * kLdsRow];
   __shared__ __attribute__((aligned(16))) h4 ls[2][2 * kTile];        // sx of the tile rows, then sw
@@ -81,9 +84,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, kh = lane >> 5;
-  const int tiles_m = (M + kTile - 1) / kTile;
-  const int m0 = (blockIdx.x % tiles_m) * kTile, n0 = (blockIdx.x / tiles_m) * kTile;
+  const int tiles_m = (M + kTile - 1) / kTile, tiles_n = (N + kTile - 1) / kTile;
+  // Split plan (rem > 0): workgroup p is piece p / rem of tile p % rem; each piece takes a
+  // contiguous range of INT4 groups, the last piece also the INT8 group.
+  const bool split_mode = rem > 0;   // uniform
+  const int lin = split_mode ? (int)blockIdx.x % rem : (int)blockIdx.x;
+  const int split = split_mode ? (int)blockIdx.x / rem : 0, nsplit = split_mode ? splits : 1;
+  const int2 tc = tile_coords(lin, tiles_m, tiles_n);
+  const int m0 = tc.x * kTile, n0 = tc.y * kTile;
   const int G = K / ATOM_GROUP;
+  const int ga = split * (G - 1) / nsplit, gb = (split + 1) * (G - 1) / nsplit;   // INT4 groups [ga, gb)
+  const bool last_split = split == nsplit - 1;
   const int klo = K - ATOM_OUTLIERS;
   const size_t rbw = (size_t)klo / 2 + ATOM_OUTLIERS;      // weight row bytes
 
@@ -219,25 +230,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   };
 
-  // INT4 groups 0 .. G-2, the next group's loads in flight during each; then the INT8 group.
-  store_stage(Int4W{}, load_stage(Int4W{}, 0), 0);
+  // INT4 groups ga .. gb-1, the next group's loads in flight during each; then (last piece)
+  // the INT8 group.  Buffer (g - ga) % 2 holds group g.
+  store_stage(Int4W{}, load_stage(Int4W{}, ga), 0);
   __syncthreads();
-  for (int g = 0; g < G - 2; ++g) {
+  for (int g = ga; g < gb - 1; ++g) {
     const Stage next = load_stage(Int4W{}, g + 1);
-    compute(Int4W{}, g, g & 1);
-    store_stage(Int4W{}, next, (g + 1) & 1);
+    compute(Int4W{}, g, (g - ga) & 1);
+    store_stage(Int4W{}, next, (g - ga + 1) & 1);
     __syncthreads();
   }
-  {
-    const int g = G - 2;
+  if (last_split) {
     const Stage next = load_stage(Int8W{}, G - 1);
-    compute(Int4W{}, g, g & 1);
-    store_stage(Int8W{}, next, (g + 1) & 1);
+    compute(Int4W{}, gb - 1, (gb - 1 - ga) & 1);
+    store_stage(Int8W{}, next, (gb - ga) & 1);
     __syncthreads();
+    compute(Int8W{}, G - 1, (gb - ga) & 1);
+  } else {
+    compute(Int4W{}, gb - 1, (gb - 1 - ga) & 1);
   }
-  compute(Int8W{}, G - 1, (G - 1) & 1);
 
   if (kAcc) return;
+  if (split_mode) {   // the piece's fp32 tile (factor 2 kept), row-major, to its scratch slot
+    float* tile = part + ((size_t)split * rem + lin) * (kTile * kTile);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = wm * 64 + i * 32 + l32;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = wn * 64 + j * 32 + q * 8 + kh * 4;
+          *reinterpret_cast<float4*>(tile + r * kTile + c) =
+              float4{yacc[i][j][4 * q], yacc[i][j][4 * q + 1], yacc[i][j][4 * q + 2], yacc[i][j][4 * q + 3]};
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int m = m0 + wm * 64 + i * 32 + l32;
@@ -266,13 +295,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }  // namespace
 
 hipError_t launch_gemm_w4a8(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M,
-                            int N, int K, uint16_t* Y, int32_t* acc, hipStream_t stream) {
-  const dim3 grid(((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile));
+                            int N, int K, uint16_t* Y, int32_t* acc, float* part, const GemmPlan& plan,
+                            hipStream_t stream) {
+  const int tiles = ((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile);
+  const bool split = !acc && plan.rem > 0 && part;
+  const dim3 grid(split ? plan.rem * plan.splits : tiles);
   if (acc)
-    hipLaunchKernelGGL(gemm_w4a8_kernel<true>, grid, dim3(kThreads), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, acc);
+    hipLaunchKernelGGL(gemm_w4a8_kernel<true>, grid, dim3(kThreads), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, acc, 0, 1,
+                       (float*)nullptr);
   else
     hipLaunchKernelGGL(gemm_w4a8_kernel<false>, grid, dim3(kThreads), 0, stream, Xq, sx, Wq, sw, M, N, K, Y,
-                       (int32_t*)nullptr);
+                       (int32_t*)nullptr, split ? plan.rem : 0, split ? plan.splits : 1, part);
+  if (split) return launch_splitk_finish(part, plan, M, N, Y, stream);
   return hipGetLastError();
 }
 

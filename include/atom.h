@@ -174,6 +174,8 @@ int atom_gemm_group_acc(const void *Xq, const void *Wq, int32_t M, int32_t N, in
  * atom_gemm_w4a8: Xq [M, K] from atom_quantize_act_a8, Wq [N, RB] from atom_pack_weights_w4a8,
  *   scales as above -> Y fp16 [M, N] = fp16_rne(sum_g acc_g * sx[g,m] * sw[g,n]), fp32 scaling.
  * atom_gemm_w4a8_group_acc: acc int32 [G, M, N] of the same operands (verification aid).
+ * atom_gemm_w4a8_workspace_bytes / atom_gemm_w4a8_ws: split-K scratch and the call that uses it,
+ *   with the semantics of atom_gemm_workspace_bytes / atom_gemm_ws (any M, including M <= 16).
  * Shapes, alignment, overlap and error rules as for the W4A4 calls.
  */
 int atom_quantize_act_a8(const void *X, const int32_t *perm, int32_t M, int32_t K, void *Xq, void *sx,
@@ -184,6 +186,9 @@ int atom_gemm_w4a8(const void *Xq, const void *sx, const void *Wq, const void *s
                    int32_t K, void *Y, void *stream);
 int atom_gemm_w4a8_group_acc(const void *Xq, const void *Wq, int32_t M, int32_t N, int32_t K, int32_t *acc,
                              void *stream);
+int64_t atom_gemm_w4a8_workspace_bytes(int32_t M, int32_t N, int32_t K);
+int atom_gemm_w4a8_ws(const void *Xq, const void *sx, const void *Wq, const void *sw, int32_t M, int32_t N,
+                      int32_t K, void *Y, void *workspace, int64_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 17
     assert sorted(bq.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -136,6 +136,13 @@ def test_w4a8_validation(lib):
     assert g(A, B, C, D, 4, 0, 256, E, S) == E_SHAPE
     assert g(A, B, C, D + 2, 4, 4, 256, E, S) == E_ALIGN
     assert g(A, B, C, D, 4, 4, 256, A + 512, S) == E_OVERLAP    # Y inside Xq (4 x 256 bytes)
+    assert lib.atom_gemm_w4a8_workspace_bytes(4, 4, 200) == -E_SHAPE
+    assert lib.atom_gemm_w4a8_workspace_bytes(16, 4096, 4096) > 0          # no few-rows kernel: splits
+    assert lib.atom_gemm_w4a8_workspace_bytes(2048, 4096, 4096) == 0
+    gw = lib.atom_gemm_w4a8_ws
+    need = lib.atom_gemm_w4a8_workspace_bytes(64, 128, 4096)
+    assert gw(A, B, C, D, 64, 128, 4096, E, E + 4, need, S) == E_ALIGN     # misaligned workspace
+    assert gw(A, B, C, D, 64, 128, 4096, E, A, need, S) == E_OVERLAP       # workspace over Xq
     ga = lib.atom_gemm_w4a8_group_acc
     assert ga(A, C, 4, 4, 256, None, S) == E_NULL
     assert ga(A, C, 4, 4, 200, E, S) == E_SHAPE

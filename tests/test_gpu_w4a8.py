@@ -147,3 +147,28 @@ def test_w4a8_zero_rows():
     assert np.all(Y[5] == 0)
     qw, swr = O.quantize_rows(wt, perm)
     assert_y_close(Y, O.gemm_ref(qx, sxr, qw, swr), "W4A8 zero rows")
+
+
+# pieces per split tile 7, 3, 2, 4 (the attention projection), 5, 6, 8, and a 16-row batch
+W8_SPLIT = [(64, 128, 4096), (200, 300, 2048), (17, 130, 1152), (256, 4096, 4096), (17, 64, 3072),
+            (40, 200, 3456), (33, 250, 4352), (16, 512, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", W8_SPLIT)
+def test_w4a8_split_k_matches_oracle(M, N, K):
+    need = bq.atom_gemm_w4a8_workspace_bytes(M, N, K)
+    assert need > 0, "this shape is expected to split"
+    _say(f"[w4a8 split-K] M={M} N={N} K={K} workspace={need}")
+    x, wt, _ = synth.make_linear(M, K, N, seed=5 * M + N + K)
+    perm = np.random.default_rng(K + 3).permutation(K).astype(np.int32)
+    Xq, sx, Wq, sw = _quantized(x, wt, perm)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")   # contents must not matter
+    Y = host(bq.atom_gemm_w4a8_ws(Xq, sx, Wq, sw, K, ws))
+    qx, sxr = O.quantize_rows(x, perm, all_int8=True)
+    qw, swr = O.quantize_rows(wt, perm)
+    assert_y_close(Y, O.gemm_ref(qx, sxr, qw, swr), f"W4A8 split {M}x{N}x{K}")
+    Y2 = host(bq.atom_gemm_w4a8_ws(Xq, sx, Wq, sw, K, ws))
+    np.testing.assert_array_equal(Y.view(np.uint16), Y2.view(np.uint16))
+    Yu = host(bq.atom_gemm_w4a8_ws(Xq, sx, Wq, sw, K, None))           # no scratch: the unsplit kernel
+    np.testing.assert_array_equal(Yu.view(np.uint16), host(bq.atom_gemm_w4a8(Xq, sx, Wq, sw, K)).view(np.uint16))
+    assert_y_close(Yu, O.gemm_ref(qx, sxr, qw, swr), f"W4A8 unsplit {M}x{N}x{K}")
