@@ -23,9 +23,10 @@
 // l & 31, element r is column (r >> 2) * 8 + (l >> 5) * 4 + (r & 3).
 //
 // Scales and epilogue.  As in the W4A4 kernel: one v_mfma_f32_32x32x8_f16 with each lane's
-// fp16 scale in K slot 0 of its half gives 2 * sx * sw exactly in the accumulator layout, the
-// int32 group sum is converted (exact below 2^24 .. here below 2^21) and added with one fp32 fma
-// per element and group; the factor 2 goes at the store.
+// fp16 scale in K slot 0 of its half gives 2 * sx * sw exactly in the accumulator layout; the
+// int32 group sum (|acc| < 2^21, so its conversion to fp32 is exact) is added with one fp32 fma
+// per element and group; the factor 2 goes at the store (or stays in a split piece's partial
+// tile, which the split-K finalize removes).
 //
 // Work layout.  One workgroup of 4 waves per 128 x 128 output tile (2 x 2 waves of 64 x 64,
 // each 2 x 2 MFMA tiles), tiles in the banded order of the W4A4 kernel; with caller scratch, a
