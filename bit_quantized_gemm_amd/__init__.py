@@ -109,22 +109,62 @@ def _check(status: int, what: str):
 
 
 # ----------------------------------------------------------------------------- tensor plumbing
+# The C ABI sees only pointers, so the sizes the kernels will read and write are checked here,
+# before the call: every tensor must have exactly the shape the entry point implies (a wrong
+# shape would otherwise be an out-of-bounds device access), the expected dtype, be contiguous
+# and live on the same ROCm device as the first operand.
 def _torch():
     import torch
     return torch
 
 
-def _dev(t, name, dtype):
+def _ptrs(*specs):
+    """Check every (tensor, name, dtype, shape) and return their device pointers.
+
+    Sizes, dtypes and contiguity of all arguments are checked first, then that they all live
+    on the first tensor's ROCm device, so a mis-sized argument is reported as such wherever it
+    lives.  ``shape=None`` skips the shape check; ``tensor=None`` passes a NULL pointer."""
     torch = _torch()
-    if not isinstance(t, torch.Tensor):
-        raise AtomError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise AtomError(f"{name} must be a ROCm device tensor (got {t.device}); there is no CPU path")
-    if t.dtype != dtype:
-        raise AtomError(f"{name} must be {dtype} (got {t.dtype})")
-    if not t.is_contiguous():
-        raise AtomError(f"{name} must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
+    for t, name, dtype, shape in specs:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise AtomError(f"{name} must be a torch.Tensor")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise AtomError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype != dtype:
+            raise AtomError(f"{name} must be {dtype} (got {t.dtype})")
+        if not t.is_contiguous():
+            raise AtomError(f"{name} must be contiguous")
+    device = None
+    out = []
+    for t, name, _, _ in specs:
+        if t is None:
+            out.append(None)
+            continue
+        if t.device.type != "cuda":
+            raise AtomError(f"{name} must be a ROCm device tensor (got {t.device}); there is no CPU path")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise AtomError(f"{name} is on {t.device}, the other operands on {device}")
+        out.append(ctypes.c_void_p(t.data_ptr()))
+    return out
+
+
+def _mat(t, name):
+    """(rows, cols) of a 2-D tensor argument."""
+    if getattr(t, "dim", lambda: -1)() != 2:
+        raise AtomError(f"{name} must be a 2-D tensor")
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def _shape_k(K):
+    """(row bytes, groups) of a valid K, else AtomError."""
+    rb, g = atom_row_bytes(K), atom_num_groups(K)
+    if rb < 0 or g < 0:
+        _check(-rb if rb < 0 else -g, f"K={K}")
+    return rb, g
 
 
 def _stream(stream, device):
@@ -140,71 +180,80 @@ def _empty(shape, dtype, like):
 # ----------------------------------------------------------------------------- entry points
 def atom_channel_stat(X, stat=None, stream=None):
     torch = _torch()
-    M, K = X.shape
+    M, K = _mat(X, "X")
     if stat is None:
         stat = _empty((K,), torch.float64, X)
-    st = load_library().atom_channel_stat(_dev(X, "X", torch.float16), M, K, _dev(stat, "stat", torch.float64),
-                                          _stream(stream, X.device))
-    _check(st, "atom_channel_stat")
+    pX, pS = _ptrs((X, "X", torch.float16, None), (stat, "stat", torch.float64, (K,)))
+    _check(load_library().atom_channel_stat(pX, M, K, pS, _stream(stream, X.device)), "atom_channel_stat")
     return stat
 
 
 def atom_select_outliers(stat, perm=None, stream=None):
     torch = _torch()
-    (K,) = stat.shape
+    if getattr(stat, "dim", lambda: -1)() != 1:
+        raise AtomError("stat must be a 1-D tensor")
+    K = int(stat.shape[0])
     if perm is None:
         perm = _empty((K,), torch.int32, stat)
-    st = load_library().atom_select_outliers(_dev(stat, "stat", torch.float64), K, _dev(perm, "perm", torch.int32),
-                                             _stream(stream, stat.device))
-    _check(st, "atom_select_outliers")
+    pS, pP = _ptrs((stat, "stat", torch.float64, None), (perm, "perm", torch.int32, (K,)))
+    _check(load_library().atom_select_outliers(pS, K, pP, _stream(stream, stat.device)), "atom_select_outliers")
     return perm
 
 
-def _rows_out(rows, K, like, q, s):
+def _row_quantize(fn, what, X, perm, q, s, stream, a8=False):
+    """Shared marshalling of the row quantize calls: X fp16 [rows, K], perm int32 [K] ->
+    codes u8 [rows, K (A8) or row bytes], scales fp16 [G, rows]."""
     torch = _torch()
-    rb = atom_row_bytes(K)
-    g = atom_num_groups(K)
-    if rb < 0 or g < 0:
-        _check(-rb if rb < 0 else -g, "shape")
+    rows, K = _mat(X, "X")
+    rb, g = _shape_k(K)
+    if a8:
+        rb = K
     if q is None:
-        q = _empty((rows, rb), torch.uint8, like)
+        q = _empty((rows, rb), torch.uint8, X)
     if s is None:
-        s = _empty((g, rows), torch.float16, like)
+        s = _empty((g, rows), torch.float16, X)
+    pX, pP, pQ, pS = _ptrs((X, "X", torch.float16, None), (perm, "perm", torch.int32, (K,)),
+                           (q, "codes", torch.uint8, (rows, rb)), (s, "scales", torch.float16, (g, rows)))
+    _check(fn(pX, pP, rows, K, pQ, pS, _stream(stream, X.device)), what)
     return q, s
 
 
 def atom_pack_weights(W, perm, Wq=None, sw=None, stream=None):
-    torch = _torch()
-    N, K = W.shape
-    Wq, sw = _rows_out(N, K, W, Wq, sw)
-    st = load_library().atom_pack_weights(_dev(W, "W", torch.float16), _dev(perm, "perm", torch.int32), N, K,
-                                          _dev(Wq, "Wq", torch.uint8), _dev(sw, "sw", torch.float16),
-                                          _stream(stream, W.device))
-    _check(st, "atom_pack_weights")
-    return Wq, sw
+    return _row_quantize(load_library().atom_pack_weights, "atom_pack_weights", W, perm, Wq, sw, stream)
 
 
 def atom_quantize_act(X, perm, Xq=None, sx=None, stream=None):
+    return _row_quantize(load_library().atom_quantize_act, "atom_quantize_act", X, perm, Xq, sx, stream)
+
+
+def _gemm_args(Xq, sx, Wq, sw, K, out, out_name, out_dtype, workspace=None, a8=False, acc=False):
+    """Check the GEMM operands against K and return (pointers, M, N, out tensor, workspace bytes).
+
+    Xq u8 [M, row bytes] (A8: [M, K]), sx fp16 [G, M], Wq u8 [N, row bytes], sw fp16 [G, N];
+    the output is fp16 Y [M, N], or int32 acc [G, M, N] (acc=True, no scales); the workspace a
+    1-D uint8 tensor or None."""
     torch = _torch()
-    M, K = X.shape
-    Xq, sx = _rows_out(M, K, X, Xq, sx)
-    st = load_library().atom_quantize_act(_dev(X, "X", torch.float16), _dev(perm, "perm", torch.int32), M, K,
-                                          _dev(Xq, "Xq", torch.uint8), _dev(sx, "sx", torch.float16),
-                                          _stream(stream, X.device))
-    _check(st, "atom_quantize_act")
-    return Xq, sx
+    rb, g = _shape_k(K)
+    M, _ = _mat(Xq, "Xq")
+    N, _ = _mat(Wq, "Wq")
+    oshape = (g, M, N) if acc else (M, N)
+    if out is None:
+        out = _empty(oshape, out_dtype, Xq)
+    if workspace is not None and getattr(workspace, "dim", lambda: -1)() != 1:
+        raise AtomError("workspace must be a 1-D uint8 tensor")
+    ptrs = _ptrs((Xq, "Xq", torch.uint8, (M, K if a8 else rb)),
+                 (None if acc else sx, "sx", torch.float16, (g, M)),
+                 (Wq, "Wq", torch.uint8, (N, rb)),
+                 (None if acc else sw, "sw", torch.float16, (g, N)),
+                 (out, out_name, out_dtype, oshape),
+                 (workspace, "workspace", torch.uint8, None))
+    return ptrs, M, N, out, (int(workspace.numel()) if workspace is not None else 0)
 
 
 def atom_gemm(Xq, sx, Wq, sw, K, Y=None, stream=None):
     torch = _torch()
-    M = Xq.shape[0]
-    N = Wq.shape[0]
-    if Y is None:
-        Y = _empty((M, N), torch.float16, Xq)
-    st = load_library().atom_gemm(_dev(Xq, "Xq", torch.uint8), _dev(sx, "sx", torch.float16),
-                                  _dev(Wq, "Wq", torch.uint8), _dev(sw, "sw", torch.float16), M, N, K,
-                                  _dev(Y, "Y", torch.float16), _stream(stream, Xq.device))
-    _check(st, "atom_gemm")
+    (pX, pSx, pW, pSw, pY, _), M, N, Y, _ = _gemm_args(Xq, sx, Wq, sw, K, Y, "Y", torch.float16)
+    _check(load_library().atom_gemm(pX, pSx, pW, pSw, M, N, K, pY, _stream(stream, Xq.device)), "atom_gemm")
     return Y
 
 
@@ -218,30 +267,17 @@ def atom_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
 def atom_gemm_ws(Xq, sx, Wq, sw, K, workspace, Y=None, stream=None):
     """atom_gemm with a caller-allocated workspace (uint8 tensor on the same device, or None)."""
     torch = _torch()
-    M = Xq.shape[0]
-    N = Wq.shape[0]
-    if Y is None:
-        Y = _empty((M, N), torch.float16, Xq)
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        ws_ptr = _dev(workspace, "workspace", torch.uint8)
-        ws_bytes = workspace.numel()
-    st = load_library().atom_gemm_ws(_dev(Xq, "Xq", torch.uint8), _dev(sx, "sx", torch.float16),
-                                     _dev(Wq, "Wq", torch.uint8), _dev(sw, "sw", torch.float16), M, N, K,
-                                     _dev(Y, "Y", torch.float16), ws_ptr, ws_bytes, _stream(stream, Xq.device))
-    _check(st, "atom_gemm_ws")
+    (pX, pSx, pW, pSw, pY, pWs), M, N, Y, nws = _gemm_args(Xq, sx, Wq, sw, K, Y, "Y", torch.float16, workspace)
+    _check(load_library().atom_gemm_ws(pX, pSx, pW, pSw, M, N, K, pY, pWs, nws, _stream(stream, Xq.device)),
+           "atom_gemm_ws")
     return Y
 
 
 def atom_gemm_group_acc(Xq, Wq, K, acc=None, stream=None):
     torch = _torch()
-    M = Xq.shape[0]
-    N = Wq.shape[0]
-    if acc is None:
-        acc = _empty((K // GROUP, M, N), torch.int32, Xq)
-    st = load_library().atom_gemm_group_acc(_dev(Xq, "Xq", torch.uint8), _dev(Wq, "Wq", torch.uint8), M, N, K,
-                                            _dev(acc, "acc", torch.int32), _stream(stream, Xq.device))
-    _check(st, "atom_gemm_group_acc")
+    (pX, _, pW, _, pA, _), M, N, acc, _ = _gemm_args(Xq, None, Wq, None, K, acc, "acc", torch.int32, acc=True)
+    _check(load_library().atom_gemm_group_acc(pX, pW, M, N, K, pA, _stream(stream, Xq.device)),
+           "atom_gemm_group_acc")
     return acc
 
 
@@ -260,52 +296,29 @@ def linear(X, perm, Wq, sw, Y=None, stream=None, workspace=None):
 # --------------------------------------------------------------------------- W4A8 variant
 def atom_quantize_act_a8(X, perm, Xq=None, sx=None, stream=None):
     """INT8 codes in every group: (Xq u8 [M, K], sx fp16 [G, M])."""
-    torch = _torch()
-    M, K = X.shape
-    _, sx = _rows_out(M, K, X, torch.empty(0), sx)
-    if Xq is None:
-        Xq = _empty((M, K), torch.uint8, X)
-    st = load_library().atom_quantize_act_a8(_dev(X, "X", torch.float16), _dev(perm, "perm", torch.int32), M, K,
-                                             _dev(Xq, "Xq", torch.uint8), _dev(sx, "sx", torch.float16),
-                                             _stream(stream, X.device))
-    _check(st, "atom_quantize_act_a8")
-    return Xq, sx
+    return _row_quantize(load_library().atom_quantize_act_a8, "atom_quantize_act_a8", X, perm, Xq, sx, stream,
+                         a8=True)
 
 
 def atom_pack_weights_w4a8(W, perm, Wq=None, sw=None, stream=None):
     """W4 rule, offset-binary INT4 layout for the W4A8 GEMM: (Wq u8 [N, RB], sw fp16 [G, N])."""
-    torch = _torch()
-    N, K = W.shape
-    Wq, sw = _rows_out(N, K, W, Wq, sw)
-    st = load_library().atom_pack_weights_w4a8(_dev(W, "W", torch.float16), _dev(perm, "perm", torch.int32), N, K,
-                                               _dev(Wq, "Wq", torch.uint8), _dev(sw, "sw", torch.float16),
-                                               _stream(stream, W.device))
-    _check(st, "atom_pack_weights_w4a8")
-    return Wq, sw
+    return _row_quantize(load_library().atom_pack_weights_w4a8, "atom_pack_weights_w4a8", W, perm, Wq, sw, stream)
 
 
 def atom_gemm_w4a8(Xq, sx, Wq, sw, K, Y=None, stream=None):
     torch = _torch()
-    M = Xq.shape[0]
-    N = Wq.shape[0]
-    if Y is None:
-        Y = _empty((M, N), torch.float16, Xq)
-    st = load_library().atom_gemm_w4a8(_dev(Xq, "Xq", torch.uint8), _dev(sx, "sx", torch.float16),
-                                       _dev(Wq, "Wq", torch.uint8), _dev(sw, "sw", torch.float16), M, N, K,
-                                       _dev(Y, "Y", torch.float16), _stream(stream, Xq.device))
-    _check(st, "atom_gemm_w4a8")
+    (pX, pSx, pW, pSw, pY, _), M, N, Y, _ = _gemm_args(Xq, sx, Wq, sw, K, Y, "Y", torch.float16, a8=True)
+    _check(load_library().atom_gemm_w4a8(pX, pSx, pW, pSw, M, N, K, pY, _stream(stream, Xq.device)),
+           "atom_gemm_w4a8")
     return Y
 
 
 def atom_gemm_w4a8_group_acc(Xq, Wq, K, acc=None, stream=None):
     torch = _torch()
-    M = Xq.shape[0]
-    N = Wq.shape[0]
-    if acc is None:
-        acc = _empty((K // GROUP, M, N), torch.int32, Xq)
-    st = load_library().atom_gemm_w4a8_group_acc(_dev(Xq, "Xq", torch.uint8), _dev(Wq, "Wq", torch.uint8), M, N, K,
-                                                 _dev(acc, "acc", torch.int32), _stream(stream, Xq.device))
-    _check(st, "atom_gemm_w4a8_group_acc")
+    (pX, _, pW, _, pA, _), M, N, acc, _ = _gemm_args(Xq, None, Wq, None, K, acc, "acc", torch.int32, a8=True,
+                                                     acc=True)
+    _check(load_library().atom_gemm_w4a8_group_acc(pX, pW, M, N, K, pA, _stream(stream, Xq.device)),
+           "atom_gemm_w4a8_group_acc")
     return acc
 
 
@@ -319,16 +332,8 @@ def atom_gemm_w4a8_workspace_bytes(M: int, N: int, K: int) -> int:
 def atom_gemm_w4a8_ws(Xq, sx, Wq, sw, K, workspace, Y=None, stream=None):
     """atom_gemm_w4a8 with a caller-allocated split-K workspace (uint8 tensor, or None)."""
     torch = _torch()
-    M = Xq.shape[0]
-    N = Wq.shape[0]
-    if Y is None:
-        Y = _empty((M, N), torch.float16, Xq)
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        ws_ptr = _dev(workspace, "workspace", torch.uint8)
-        ws_bytes = workspace.numel()
-    st = load_library().atom_gemm_w4a8_ws(_dev(Xq, "Xq", torch.uint8), _dev(sx, "sx", torch.float16),
-                                          _dev(Wq, "Wq", torch.uint8), _dev(sw, "sw", torch.float16), M, N, K,
-                                          _dev(Y, "Y", torch.float16), ws_ptr, ws_bytes, _stream(stream, Xq.device))
-    _check(st, "atom_gemm_w4a8_ws")
+    (pX, pSx, pW, pSw, pY, pWs), M, N, Y, nws = _gemm_args(Xq, sx, Wq, sw, K, Y, "Y", torch.float16, workspace,
+                                                           a8=True)
+    _check(load_library().atom_gemm_w4a8_ws(pX, pSx, pW, pSw, M, N, K, pY, pWs, nws, _stream(stream, Xq.device)),
+           "atom_gemm_w4a8_ws")
     return Y

@@ -22,10 +22,12 @@
 // combined with DPP row operations.  Each thread writes its 16 codes as 8 bytes (INT4) or
 // 16 bytes (INT8 tail), so a group's 8 lanes store one contiguous 64- or 128-byte run.
 //
-// Exact codes without a per-element IEEE division: with r = 1/s correctly rounded,
-// t = x*r, e = fma(-t, s, x), u = fma(e, r, t), the integer nearest u (ties to even) equals
-// the integer nearest the correctly rounded fp32 quotient x/s for every fp16 x and every
-// fp16 scale s this rule can produce (checked over all 2.0e9 such pairs on the CPU).  The
+// Exact codes without a per-element IEEE division (a Markstein-style quotient correction):
+// with r = 1/s correctly rounded, t = x*r, e = fma(-t, s, x) (the remainder, rounded once)
+// and u = fma(e, r, t), the integer nearest clamp(u) (ties to even) equals the clamped integer
+// nearest the correctly rounded fp32 quotient x/s for every fp16 scale s this rule can produce
+// and every fp16 x up to the largest absmax giving that scale (tests/quotient_exhaustive.c
+// walks all 1.8e9 such pairs for both qmax with IEEE fused multiply-adds on the CPU).  The
 // scale itself and r come from a reciprocal and one correction step each, not from an IEEE
 // divide (exact for every fp16 input, see quantize16).  INT8 codes: adding 1.5*2^23 rounds
 // the clamped value to that integer with ties to even and leaves its two's-complement low

@@ -61,10 +61,16 @@ enum {
   ATOM_E_HIP = 5       /* the HIP runtime reported an error when enqueuing */
 };
 
-/* Bytes of one packed row, (K-128)/2 + 128; or -ATOM_E_SHAPE for an invalid K. */
+/* Bytes of one packed row, (K-128)/2 + 128: the K-128 bulk channels at four bits each and
+ * the 128 outlier channels at eight (record, Fields "Bits": w4a4 with the outlier channels at
+ * higher precision, and "notes": one 128-channel high-precision group); or -ATOM_E_SHAPE for
+ * an invalid K.  Pure host function, no HIP call. */
 int64_t atom_row_bytes(int32_t K);
 
-/* Number of 128-channel groups, K/128; or -ATOM_E_SHAPE for an invalid K. */
+/* Number of 128-channel groups, K/128, each with its own scale (record, Field "Weight group
+ * size" and "notes": every contiguous run of 128 elements is quantized independently); groups
+ * 0..G-2 are INT4, group G-1 is the INT8 outlier group.  -ATOM_E_SHAPE for an invalid K.  Pure
+ * host function, no HIP call. */
 int32_t atom_num_groups(int32_t K);
 
 /* Static description of a status code; never NULL. */

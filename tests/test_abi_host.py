@@ -226,3 +226,73 @@ def test_gemm_ws_validation(lib):
     assert g(A, B, C, D, M, N, K, E, F + 8, need, S) == E_ALIGN       # workspace used, misaligned
     assert g(A, B, C, D, M, N, K, E, E + 64, need, S) == E_OVERLAP    # workspace over Y
     assert g(A, B, C, D, M, N, K, E, A + 16, need, S) == E_OVERLAP    # workspace over Xq
+
+
+class _NoLaunch:
+    """Stands in for the loaded library: the size helpers pass through, every entry point that
+    would enqueue work fails the test if it is ever reached."""
+
+    def __init__(self, lib):
+        self._lib = lib
+
+    def __getattr__(self, name):
+        if name in ("atom_row_bytes", "atom_num_groups", "atom_strerror", "atom_gemm_workspace_bytes",
+                    "atom_gemm_w4a8_workspace_bytes"):
+            return getattr(self._lib, name)
+
+        def fail(*a):
+            raise AssertionError(f"{name} was called with arguments the binding should have refused")
+        return fail
+
+
+def test_binding_rejects_mis_sized_tensors(lib, monkeypatch):
+    """The C ABI cannot see buffer sizes, so the binding checks every tensor's shape against the
+    sizes the call implies before calling it; a mis-sized tensor raises AtomError and nothing is
+    enqueued (no entry point is reached)."""
+    torch = pytest.importorskip("torch")
+    monkeypatch.setattr(bq, "_LIB", _NoLaunch(lib))
+    M, N, K = 4, 6, 384
+    rb, G = bq.atom_row_bytes(K), bq.atom_num_groups(K)
+    u8, f16, i32, f64 = torch.uint8, torch.float16, torch.int32, torch.float64
+    z = torch.zeros
+    X, W, perm = z((M, K), dtype=f16), z((N, K), dtype=f16), z((K,), dtype=i32)
+    Xq, sx, Wq, sw = z((M, rb), dtype=u8), z((G, M), dtype=f16), z((N, rb), dtype=u8), z((G, N), dtype=f16)
+    bad = [
+        # quantize / pack outputs and perm
+        lambda: bq.atom_quantize_act(X, z((K - 1,), dtype=i32)),
+        lambda: bq.atom_quantize_act(X, perm, Xq=z((M, rb - 1), dtype=u8)),
+        lambda: bq.atom_quantize_act(X, perm, sx=z((M, G), dtype=f16)),
+        lambda: bq.atom_pack_weights(W, perm, Wq=z((N + 1, rb), dtype=u8)),
+        lambda: bq.atom_quantize_act_a8(X, perm, Xq=z((M, rb), dtype=u8)),          # A8 rows are K bytes
+        lambda: bq.atom_pack_weights_w4a8(W, perm, sw=z((G, N - 1), dtype=f16)),
+        lambda: bq.atom_channel_stat(X, stat=z((K + 1,), dtype=f64)),
+        lambda: bq.atom_select_outliers(z((K,), dtype=f64), perm=z((K - 2,), dtype=i32)),
+        # GEMM operands against K
+        lambda: bq.atom_gemm(Xq, sx, Wq, sw, K + 128),
+        lambda: bq.atom_gemm(z((M, K), dtype=u8), sx, Wq, sw, K),                   # an A8 Xq to the W4A4 GEMM
+        lambda: bq.atom_gemm(Xq, z((G, M + 1), dtype=f16), Wq, sw, K),
+        lambda: bq.atom_gemm(Xq, sx, Wq, z((G - 1, N), dtype=f16), K),
+        lambda: bq.atom_gemm(Xq, sx, z((N, rb + 16), dtype=u8), sw, K),
+        lambda: bq.atom_gemm(Xq, sx, Wq, sw, K, Y=z((N, M), dtype=f16)),
+        lambda: bq.atom_gemm_ws(Xq, sx, Wq, sw, K, z((8, 8), dtype=u8)),           # 2-D workspace
+        lambda: bq.atom_gemm_ws(Xq, sx, Wq, sw, K, z((64,), dtype=u8), Y=z((M, N + 1), dtype=f16)),
+        lambda: bq.atom_gemm_group_acc(Xq, Wq, K, acc=z((G, M, N - 1), dtype=i32)),
+        lambda: bq.atom_gemm_w4a8(Xq, sx, Wq, sw, K),                               # a W4A4 Xq to the W4A8 GEMM
+        lambda: bq.atom_gemm_w4a8_group_acc(z((M, K), dtype=u8), Wq, K, acc=z((G + 1, M, N), dtype=i32)),
+        lambda: bq.atom_gemm_w4a8_ws(z((M, K), dtype=u8), sx, Wq, sw, K, None, Y=z((M,), dtype=f16)),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(bq.AtomError, match="shape|2-D|1-D"):
+            call()
+    # wrong dtype, and a non-contiguous tensor
+    with pytest.raises(bq.AtomError, match="must be torch.float16"):
+        bq.atom_gemm(Xq, sx.float(), Wq, sw, K)
+    with pytest.raises(bq.AtomError, match="contiguous"):
+        bq.atom_gemm(Xq, sx, Wq, sw, K, Y=z((N, M), dtype=f16).t())
+    with pytest.raises(bq.AtomError, match="K=200"):
+        bq.atom_gemm(Xq, sx, Wq, sw, 200)
+    # correctly sized host tensors get as far as the device check, still without a call
+    with pytest.raises(bq.AtomError, match="ROCm device"):
+        bq.atom_gemm(Xq, sx, Wq, sw, K)
+    with pytest.raises(bq.AtomError, match="ROCm device"):
+        bq.atom_gemm_w4a8_ws(z((M, K), dtype=u8), sx, Wq, sw, K, z((16,), dtype=u8))

@@ -172,7 +172,21 @@ def test_p3_lossless_power_of_two_scales(K):
     y64 = O.gemm_ref_grouped(qx, sx, qw, sw)
     textbook = X.astype(np.float64) @ W.astype(np.float64).T
     np.testing.assert_array_equal(y64, textbook)
+    np.testing.assert_array_equal(O.gemm_ref(qx, sx, qw, sw), textbook)
     assert np.array_equal(O.unpack_rows(O.pack_rows(qx), K), qx)
+    # the layer's two calls: packed codes decode to the known codes, scales are the known ones
+    xq, sx2 = O.quantize_act(X, perm)
+    wq, sw2 = O.pack_weights(W, perm)
+    np.testing.assert_array_equal(O.unpack_rows(xq, K), qx_true)
+    np.testing.assert_array_equal(O.unpack_rows(wq, K), qw_true)
+    np.testing.assert_array_equal(sx2.astype(np.float64).T, sx_true)
+    np.testing.assert_array_equal(sw2.astype(np.float64).T, sw_true)
+    # and the whole layer: Y64 is the textbook product, Y16 its fp16 rounding
+    y16, y64b, (xq3, _), (wq3, _) = O.linear(X, W, perm)
+    np.testing.assert_array_equal(y64b, textbook)
+    np.testing.assert_array_equal(xq3, xq)
+    np.testing.assert_array_equal(wq3, wq)
+    np.testing.assert_array_equal(y16, textbook.astype(np.float16))
 
 
 # --------------------------------------------------------------------------- P4 in-group permutation invariance
@@ -210,6 +224,39 @@ def test_p5_effective_bits(K, expected):
     assert measured == pytest.approx(((K - 128) * 4 + 128 * 8 + (K // 128) * 16) / K, abs=1e-12)
     if K >= 4096:
         assert round(measured) == 4
+
+
+@pytest.mark.parametrize("K,fp16_scales,fp32_scales", [(1024, 4.625, 4.75), (4096, 4.25, 4.375),
+                                                       (8192, 4.1875, 4.3125), (11008, 4.1715, 4.2965)])
+def test_p5_effective_bits_closed_form(K, fp16_scales, fp32_scales):
+    """effective_bits against the bit-accounting table (INT4 bulk at 4 bits, the 128-channel
+    group at 8 bits, one scale per 128-group; fp16 scales as stored, fp32 for comparison)."""
+    assert O.effective_bits(K) == pytest.approx(fp16_scales, abs=5e-5)
+    assert O.effective_bits(K, scale_bytes=4) == pytest.approx(fp32_scales, abs=5e-5)
+    assert O.effective_bits(K) - O.effective_bits(K, scale_bytes=4) == pytest.approx(-16 / 128)
+
+
+def test_to_fp16_rounds_once_to_nearest_even():
+    """Y16 = fp16_rne(Y64) in one rounding, values worked out from the binary16 format: 11
+    significant bits, largest finite 65504, subnormal spacing 2^-24."""
+    u = 2.0 ** -10                                  # fp16 spacing on [1, 2)
+    cases = [
+        (1.0 + u / 2, 1.0),                         # tie -> even (1.0)
+        (1.0 + 3 * u / 2, 1.0 + 2 * u),             # tie -> even (1 + 2u)
+        (1.0 + u / 2 + 2.0 ** -40, 1.0 + u),        # just above the tie: up (a detour through fp32 would give 1.0)
+        (-(1.0 + u / 2 + 2.0 ** -40), -(1.0 + u)),
+        (65504.0, 65504.0),
+        (65519.99, 65504.0),                        # below the overflow threshold 65520
+        (65520.0, np.inf),                          # the tie above 65504 rounds to even = overflow
+        (2.0 ** -25, 0.0),                          # half the smallest subnormal: tie -> even (0)
+        (2.0 ** -25 + 2.0 ** -60, 2.0 ** -24),
+        (3 * 2.0 ** -25, 2.0 ** -23),               # tie between 1 and 2 subnormal steps -> 2
+        (0.1, 0.0999755859375),                     # nearest fp16 to 0.1 (0x2E66)
+    ]
+    y = O.to_fp16(np.array([c[0] for c in cases], dtype=np.float64))
+    assert y.dtype == np.float16
+    for (v, want), got in zip(cases, y.astype(np.float64)):
+        assert got == want, (v, got, want)
 
 
 # --------------------------------------------------------------------------- P6 a-priori error bound (quality)

@@ -116,3 +116,44 @@ def test_w4a8_group_products_and_output_brute_force(M, N, K):
     y64 = O.gemm_ref(qx, sx, qw, sw)
     exact = np.array([[float(v) for v in r] for r in y])
     assert np.allclose(y64, exact, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("K", [256, 1152])
+def test_w4a8_layer_calls_lossless_power_of_two_scales(K):
+    """The variant's two calls on inputs built as s * q (power-of-two s per group, max|q| =
+    qmax in every group): quantize_act_a8 must return every code as its two's-complement byte
+    (INT8 in EVERY group, qmax 127) and the known scales; pack_weights_w4a8 the known W4 codes
+    (INT4 bulk, INT8 last group) in the offset-binary layout whose bytes the hand-derived
+    fixture pins.  A packer mix-up, a missing all-groups-INT8 switch or fp32-sized scales fail."""
+    rng = np.random.default_rng(K + 5)
+    G = K // 128
+
+    def build(rows, qmaxes):
+        q = np.concatenate([rng.integers(-qm, qm + 1, size=(rows, 128)) for qm in qmaxes], axis=1)
+        s = np.ldexp(1.0, rng.integers(-12, 2, size=(rows, G)))
+        for g, qm in enumerate(qmaxes):
+            q[np.arange(rows), g * 128 + rng.integers(0, 128, size=rows)] = qm * rng.choice([-1, 1], size=rows)
+        return (q.reshape(rows, G, 128) * s[:, :, None]).reshape(rows, K).astype(np.float16), q.astype(np.int8), s
+
+    X, qx_true, sx_true = build(6, [127] * G)
+    W, qw_true, sw_true = build(9, [7] * (G - 1) + [127])
+    perm = np.arange(K, dtype=np.int32)
+    xb, sx = O.quantize_act_a8(X, perm)
+    assert xb.dtype == np.uint8 and xb.shape == (6, K)
+    assert sx.dtype == np.float16 and sx.shape == (G, 6)
+    np.testing.assert_array_equal(xb.view(np.int8), qx_true)
+    np.testing.assert_array_equal(sx.astype(np.float64).T, sx_true)
+    wb, sw = O.pack_weights_w4a8(W, perm)
+    assert wb.dtype == np.uint8 and wb.shape == (9, O.row_bytes(K))
+    assert sw.dtype == np.float16 and sw.shape == (G, 9)
+    np.testing.assert_array_equal(O.unpack_rows_w4a8(wb, K), qw_true)
+    np.testing.assert_array_equal(sw.astype(np.float64).T, sw_true)
+    # byte-level: code k of the body in byte 4 (k // 8) + k % 4, biased by 8 (fixture layout)
+    k = np.arange(K - 128)
+    b = wb[:, 4 * (k // 8) + (k % 4)].astype(np.int16)
+    nib = np.where(k % 8 >= 4, b >> 4, b & 15) - 8
+    np.testing.assert_array_equal(nib, qw_true[:, :K - 128])
+    np.testing.assert_array_equal(wb[:, (K - 128) // 2:].view(np.int8), qw_true[:, K - 128:])
+    # the output of the variant: exact textbook product
+    y64 = O.gemm_ref(xb.view(np.int8), sx, O.unpack_rows_w4a8(wb, K), sw)
+    np.testing.assert_array_equal(y64, X.astype(np.float64) @ W.astype(np.float64).T)

@@ -15,6 +15,7 @@ Every claim is checked with exact rational arithmetic: fp32 and fp16 rounding ar
 here (round to nearest, ties to even), the fused operations round once.
 """
 from fractions import Fraction as F
+import os
 import struct
 
 import numpy as np
@@ -95,3 +96,45 @@ def test_biased_fp16_rounding_gives_integer_code_ties_to_even():
         rem = u - fl
         want = fl + 1 if rem > F(1, 2) or (rem == F(1, 2) and fl % 2 == 1) else fl
         assert n == want, (float(u), n, want)
+
+
+# --------------------------------------------------------------------------- the code quotient, exhaustively
+def _reachable_scales(qmax):
+    """(scale, largest absmax with that scale) for every fp16 absmax a >= 0, as fp16 bit
+    patterns: s = fp16_rne(fl32(a / qmax)) (numpy's fp32 division and fp32 -> fp16 conversion
+    are IEEE round to nearest even)."""
+    a = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)            # 0 and every positive finite fp16
+    s = (a.astype(np.float32) / np.float32(qmax)).astype(np.float16).view(np.uint16)
+    # s is non-decreasing in a, so the last a of each run of equal s is that scale's largest absmax
+    last = np.nonzero(np.append(s[1:] != s[:-1], True))[0]
+    return np.stack([s[last], a.view(np.uint16)[last]], axis=1).astype(np.uint16)
+
+
+@pytest.mark.parametrize("qmax", [7, 127])
+def test_code_quotient_exhaustive(qmax, tmp_path):
+    """rint(clamp(u)) with u = fma(fma(-t, s, x), r, t), t = fl32(x * r), r = fl32(1/s), equals
+    clamp(rint(fl32(x / s))) for every reachable fp16 scale s and every fp16 x with |x| at most
+    the largest absmax that produces s: about 0.9 * 10^9 pairs per qmax, checked by a C program with
+    IEEE binary32 fused multiply-adds (tests/quotient_exhaustive.c)."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quotient_exhaustive.c")
+    exe = str(tmp_path / "quotient_exhaustive")
+    subprocess.run([gcc, "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", src, "-o", exe, "-lm"],
+                   check=True)
+    pairs = _reachable_scales(qmax)
+    assert pairs[0, 0] == 0 and pairs[-1, 1] == 0x7BFF        # zero scale first, fp16 max last
+    payload = struct.pack("<ii", qmax, len(pairs)) + pairs.tobytes()
+    env = dict(os.environ, OMP_NUM_THREADS=str(min(8, os.cpu_count() or 1)))
+    r = subprocess.run([exe], input=payload, capture_output=True, env=env, timeout=600)
+    out = r.stdout.decode()
+    assert r.returncode == 0, out + r.stderr.decode()
+    n = int(out.split()[1])
+    # the whole domain was walked: x = +-0 .. +-absmax for every scale (positive fp16 bit
+    # patterns are ordered like their values)
+    assert n == 2 * int((pairs[:, 1].astype(np.int64) + 1).sum()), out
+    assert "mismatches 0" in out, out
