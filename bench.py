@@ -100,44 +100,182 @@ class _nullctx:
         return False
 
 
-def cpu_baseline(shapes, budget_rows, a8=False):
-    """Time the CPU oracle (quantize + dequantise-then-fp64-matmul) on a row sample of every
-    shape; weights are packed by the oracle beforehand, like the GPU path.  a8: INT8 codes in
-    every activation group (the W4A8 variant)."""
+def _cpu_threads():
+    """Threads for the oracle: every CPU in this process's affinity, capped by OMP_NUM_THREADS
+    when the environment sets it (the GPU machine sets it to 16, its CPU share per GPU)."""
+    aff = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    cap = int(env) if env and env.isdigit() and int(env) > 0 else None
+    n = min(aff, cap) if cap else aff
+    why = (f"capped at OMP_NUM_THREADS={cap}, the box's CPU share" if cap and cap < aff
+           else "every CPU in the affinity mask")
+    return n, aff, why
+
+
+def cpu_baseline(sets, budget_rows, a8=False, reps=3):
+    """Time the CPU oracle (quantize + dequantise-then-fp64-matmul + fp16 rounding) on the first
+    rows of every shape (median of `reps` runs), with weights packed by the oracle beforehand,
+    like the GPU path.  a8: INT8 codes in every activation group (the W4A8 variant).
+
+    Returns (baseline dict, oracle outputs per shape for the parity check of the GPU run)."""
     import synth
     from oracle import atom_oracle as O
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
     except Exception:                                      # pragma: no cover
         threadpool_limits = None
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    cores, aff, why = _cpu_threads()
     ops = 0
     secs = 0.0
     parts = []
     blas = None
+    ref = {}
     with (threadpool_limits(limits=cores) if threadpool_limits else _nullctx()):
-        for key in shapes:
-            w = synth.get(key)
+        for s in sets:
+            w = s["w"]
             x, wt, _ = synth.make_inputs(w)
             rows = min(w.M, budget_rows)
             perm = O.outlier_perm(x)
             qw, sw = O.quantize_rows(wt, perm)
             xs = np.ascontiguousarray(x[:rows])
-            t0 = time.perf_counter()
-            qx, sx = O.quantize_rows(xs, perm, all_int8=a8)
-            y = O.to_fp16(O.gemm_ref(qx, sx, qw, sw))
-            dt = time.perf_counter() - t0
-            assert y.shape == (rows, w.N)
+            times = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                qx, sx = O.quantize_rows(xs, perm, all_int8=a8)
+                y64 = O.gemm_ref(qx, sx, qw, sw)
+                y16 = O.to_fp16(y64)
+                times.append(time.perf_counter() - t0)
+            dt = float(np.median(times))
+            assert y16.shape == (rows, w.N)
             ops += 2 * rows * w.N * w.K
             secs += dt
-            parts.append(f"{key}: first {rows} of {w.M} rows x N={w.N} x K={w.K} in {dt:.2f}s")
+            what = "every" if rows == w.M else f"the first {rows} of {w.M}"
+            parts.append(f"{w.key}: {what} rows x N={w.N} x K={w.K} in {dt:.2f}s (median of {reps})")
             log(f"[cpu] {parts[-1]}")
+            ref[w.key] = dict(rows=rows, perm=perm, x=xs, qx=qx, sx=sx, qw=qw, sw=sw, y64=y64)
         if threadpool_limits:
             info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
             blas = f'{info[0].get("internal_api")} x{info[0].get("num_threads")}' if info else None
-    return {"value": ops / secs / 1e12, "unit": "TOP/s", "cores": cores, "kind": "oracle",
+    base = {"value": ops / secs / 1e12, "unit": "TOP/s", "cores": cores, "kind": "oracle",
             "sample": "; ".join(parts) + f"; numpy oracle, BLAS {blas}, {cores} threads",
-            "seconds": round(secs, 3)}
+            "seconds": round(secs, 3), "affinity_cpus": aff, "threads_rule": why}
+    return base, ref
+
+
+def parity_vs_oracle(sets, ref, a8=False):
+    """Compare the GPU outputs of input copy 0 (the unmodified synthetic inputs) with the oracle
+    outputs of the CPU leg: perm, packed weights and their scales, packed activation codes and
+    scales bit-exact; Y within max(2e-3 |Y64|, 1e-2) of the oracle's fp64 value."""
+    from oracle import atom_oracle as O
+    out = {}
+    ok = True
+    for s in sets:
+        w = s["w"]
+        r = ref[w.key]
+        rows = r["rows"]
+        c = s["copies"][0]
+        pack_x = O.pack_rows_a8 if a8 else O.pack_rows
+        pack_w = O.pack_rows_w4a8 if a8 else O.pack_rows
+        xq = c["Xq"][:rows].cpu().numpy()
+        sx = c["sx"][:, :rows].cpu().numpy()
+        y = c["Y"][:rows].cpu().numpy().astype(np.float64)
+        err = np.abs(y - r["y64"])
+        tol = np.maximum(2e-3 * np.abs(r["y64"]), 1e-2)
+        d = {
+            "rows": rows,
+            "perm": bool(np.array_equal(s["perm"].cpu().numpy(), r["perm"])),
+            "weights": bool(np.array_equal(c["Wq"].cpu().numpy(), pack_w(r["qw"]))
+                            and np.array_equal(c["sw"].cpu().numpy().view(np.uint16), r["sw"].view(np.uint16))),
+            "codes": bool(np.array_equal(xq, pack_x(r["qx"]))),
+            "scales": bool(np.array_equal(sx.view(np.uint16), r["sx"].view(np.uint16))),
+            "y_within_tol": bool(np.all(err <= tol)),
+            "y_max_abs_err": float(err.max()),
+            "y_max_err_over_tol": float((err / tol).max()),
+        }
+        ok = ok and d["perm"] and d["weights"] and d["codes"] and d["scales"] and d["y_within_tol"]
+        out[w.key] = d
+    out["ok"] = ok
+    return out
+
+
+def hbm_copy_gbs(torch, dev, mib=1024, reps=10):
+    """Bandwidth of a plain device-to-device copy of `mib` MiB (read + write bytes / time), the
+    practical streaming rate of this GPU next to the 8 TB/s specification."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(2):
+        dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return round(2 * n / (ms * 1e-3) / 1e9, 1)
+
+
+class ClockSampler:
+    """Samples the GPU's current graphics clock (amdsmi) from a thread while work runs."""
+
+    def __init__(self, index=0, period_s=0.002):
+        self.samples, self.err, self.period = [], None, period_s
+        self._stop = False
+        self._h = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[index]
+        except Exception as e:                               # pragma: no cover
+            self.err = f"amdsmi unavailable: {e}"
+
+    def _read(self):
+        smi = self._smi
+        try:
+            m = smi.amdsmi_get_gpu_metrics_info(self._h)
+            for k in ("current_gfxclk", "average_gfxclk_frequency"):
+                v = m.get(k)
+                if isinstance(v, (list, tuple)):
+                    v = [u for u in v if isinstance(u, (int, float)) and 0 < u < 10000]
+                    v = float(np.mean(v)) if v else None
+                if isinstance(v, (int, float)) and 0 < v < 10000:
+                    return float(v)
+        except Exception:
+            pass
+        c = smi.amdsmi_get_clock_info(self._h, smi.AmdSmiClkType.GFX)
+        return float(c["clk"])
+
+    def __enter__(self):
+        import threading
+        if self._h is None:
+            return self
+
+        def run():
+            while not self._stop:
+                try:
+                    self.samples.append(self._read())
+                except Exception as e:                       # pragma: no cover
+                    self.err = str(e)
+                    return
+                time.sleep(self.period)
+        self._t = threading.Thread(target=run, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *a):
+        self._stop = True
+        if self._h is not None:
+            self._t.join()
+        return False
+
+    def median_mhz(self):
+        return float(np.median(self.samples)) if self.samples else None
 
 
 def quant_only(args, torch, bq, synth, dev, R):
@@ -306,6 +444,21 @@ def main():
                              quant_us_p10_50_90=[round(1e3 * float(v), 2) for v in np.percentile(q, [10, 50, 90])],
                              gemm_us_p10_50_90=[round(1e3 * float(v), 2) for v in np.percentile(g, [10, 50, 90])])
 
+    # ---------------------------------------------------------------- clock under load, copy bandwidth
+    # (outside the timed region) the graphics clock sampled while the same steps run for ~0.5 s,
+    # and the rate of a plain device copy
+    with ClockSampler() as clk:
+        t_end_clk = time.perf_counter() + 0.5
+        i = 0
+        while time.perf_counter() < t_end_clk:
+            step(i)
+            i += 1
+            if i % 50 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+    sclk = clk.median_mhz()
+    copy_gbs = hbm_copy_gbs(torch, dev)
+
     ops_step = sum(s["w"].ops for s in sets)
     value = ops_step / (ms_per_step * 1e-3) / 1e12
 
@@ -382,10 +535,22 @@ def main():
         },
         "shapes": shapes,
     }
+    line["measured"] = {
+        "sclk_mhz_under_load": sclk, "sclk_samples": len(clk.samples), "sclk_error": clk.err,
+        "int8_peak_tops_at_sclk": round(256 * sclk * 1e6 * 8192 / 1e12, 1) if sclk else None,
+        "fp6_peak_tops_at_sclk": round(256 * sclk * 1e6 * 16384 / 1e12, 1) if sclk else None,
+        "gemm_frac_fp6_peak_at_sclk": round(gemm_tops / (256 * sclk * 1e6 * 16384 / 1e12), 4) if sclk else None,
+        "hbm_copy_gbs": copy_gbs,
+    }
     if not args.no_cpu_baseline:
-        log("[cpu] timing the oracle on a row sample")
-        line["cpu_baseline"] = cpu_baseline(keys, args.cpu_rows, a8=w4a8)
+        log("[cpu] timing the oracle on the same workload")
+        base, ref = cpu_baseline(sets, args.cpu_rows, a8=w4a8)
+        line["cpu_baseline"] = base
+        line["parity"] = parity_vs_oracle(sets, ref, a8=w4a8)
+        log(f"[parity] {'ok' if line['parity']['ok'] else 'FAILED'}")
     print(json.dumps(line), flush=True)
+    if "parity" in line and not line["parity"]["ok"]:
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -65,8 +65,12 @@ hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq,
 // Few-rows kernel (M <= kSmallMaxM), Y written directly.
 hipError_t launch_gemm_small(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M,
                              int N, int K, uint16_t* Y, hipStream_t stream);
+// Per-group integer sums [G, M, N] from the kernel atom_gemm runs for this shape (the few-rows
+// kernel for M <= kSmallMaxM, the tiled kernel otherwise).
 hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K, int32_t* acc,
                                  hipStream_t stream);
+hipError_t launch_gemm_small_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K, int32_t* acc,
+                                       hipStream_t stream);
 // W4A8 GEMM (gemm_w4a8.hip): Xq in kRowA8 rows, Wq in kRowW4A8 rows.  acc != nullptr: write
 // the per-group int32 accumulators [G, M, N] instead of Y.
 // plan: gemm_plan_tiled(M, N, K), or an unsplit plan; `part` holds gemm_workspace_bytes(plan)

@@ -607,6 +607,7 @@ hipError_t launch_splitk_finish(const float* part, const GemmPlan& plan, int M, 
 
 hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K, int32_t* acc,
                                  hipStream_t stream) {
+  if (gemm_plan(M, N, K).small) return launch_gemm_small_group_acc(Xq, Wq, M, N, K, acc, stream);
   const dim3 grid(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM));
   hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, true>), grid, dim3(kWavesM * kWavesN * 64), 0,
                      stream, Xq, (const uint16_t*)nullptr, Wq, (const uint16_t*)nullptr, M, N, K,

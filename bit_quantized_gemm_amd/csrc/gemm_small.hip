@@ -68,13 +68,16 @@ __device__ __forceinline__ h4 scale_operand(uint16_t v) {
 constexpr int kMaxWaves = 16;                // waves (K ranges in flight) per workgroup
 
 // blockIdx.x: column block (columns n0 = 16 blockIdx.x ..); wave w handles K ranges w, w + waves, ...
-template <int MAXG>
+// kAcc = true: write each group's exact integer sums to acc_out [G, M, N] instead of Y (the
+// same loads, decode and MFMAs; no scales are read).
+template <int MAXG, bool kAcc>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const uint8_t* __restrict__ Xq,
                                                                          const uint16_t* __restrict__ sx,
                                                                          const uint8_t* __restrict__ Wq,
                                                                          const uint16_t* __restrict__ sw, int M,
                                                                          int N, int K, int ranges,
-                                                                         uint16_t* __restrict__ Y) {
+                                                                         uint16_t* __restrict__ Y,
+                                                                         int32_t* __restrict__ acc_out) {
   __shared__ v4f red[kMaxWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
   const int r = lane & 15, slice = lane >> 4;
@@ -85,6 +88,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
   const int n = min(n0 + r, N - 1), m = min(r, M - 1);
   const uint8_t* wrow = Wq + (size_t)n * rb + 16 * slice;
   const uint8_t* xrow = Xq + (size_t)m * rb + 16 * slice;
+  const int c0 = n0 + 4 * slice;                     // this lane's first output column
+  // kAcc: this lane's sums of group g are token row r, columns c0 .. c0 + 3
+  auto store_acc = [&](int g, v4f a) {
+    if (r >= M) return;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (c0 + j < N) acc_out[((size_t)g * M + r) * N + c0 + j] = (int32_t)a[j];   // exact integers
+  };
 
   v4f yacc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int range = wave; range < ranges; range += waves) {
@@ -102,8 +113,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
       const int g = min(ga + i, gb - 1);
       wl[i] = *reinterpret_cast<const uint4*>(wrow + (size_t)g * 64);
       xl[i] = *reinterpret_cast<const uint4*>(xrow + (size_t)g * 64);
-      wsc[i] = sw[(size_t)g * N + n];
-      xsc[i] = sx[(size_t)g * M + m];
+      if (!kAcc) {
+        wsc[i] = sw[(size_t)g * N + n];
+        xsc[i] = sx[(size_t)g * M + m];
+      }
     }
     // INT8 outlier group: the 16-byte K slice of each 64-byte half
     const size_t o8 = last ? rb - ATOM_OUTLIERS : (size_t)ga * 64;
@@ -115,7 +128,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
       w8[c] = *reinterpret_cast<const v4i*>(Wq + (size_t)n * rb + o8 + 16 * slice + c8 * c);
       x8[c] = *reinterpret_cast<const v4i*>(Xq + (size_t)m * rb + o8 + 16 * slice + c8 * c);
     }
-    const uint16_t wsc8 = sw[(size_t)g8 * N + n], xsc8 = sx[(size_t)g8 * M + m];
+    const uint16_t wsc8 = kAcc ? (uint16_t)0 : sw[(size_t)g8 * N + n];
+    const uint16_t xsc8 = kAcc ? (uint16_t)0 : sx[(size_t)g8 * M + m];
     __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the first use
     // Branch-free as well (a load used only under a branch gets sunk into it): a repeated
     // group gets a zero scale product and adds exactly +0.
@@ -125,6 +139,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
       const v8i b = fp6_operand(xl[i]);
       // cbsz = blgp = 2: both operands fp6 e2m3
       const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{}, 2, 2, 0, kScaleE8M0, 0, kScaleE8M0);
+      if (kAcc) {
+        if (i < ng) store_acc(ga + i, acc);
+        continue;
+      }
       const uint16_t ws = i < ng ? wsc[i] : (uint16_t)0;
       const v4f sp = __builtin_amdgcn_mfma_f32_16x16x16f16(scale_operand(ws), scale_operand(xsc[i]), v4f{}, 0, 0, 0);
 #pragma unroll
@@ -133,6 +151,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
     {   // INT8 group, counted by the last range only (zero scale product elsewhere)
       v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8[0], x8[0], v4i{}, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8[1], x8[1], acc, 0, 0, 0);
+      if (kAcc) {
+        if (last) store_acc(G - 1, v4f{(float)acc[0], (float)acc[1], (float)acc[2], (float)acc[3]});
+        continue;
+      }
       const uint16_t ws = last ? wsc8 : (uint16_t)0;
       const v4f sp = __builtin_amdgcn_mfma_f32_16x16x16f16(scale_operand(ws), scale_operand(xsc8), v4f{}, 0, 0, 0);
 #pragma unroll
@@ -140,6 +162,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
     }
   }
 
+  if (kAcc) return;
   red[wave][lane] = yacc;
   __syncthreads();
   if (wave != 0) return;
@@ -151,7 +174,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
   }
   // lane: token row r, columns n0 + 4 slice .. + 3; the factor 4 of the scale products goes
   if (r >= M) return;
-  const int c0 = n0 + 4 * slice;
   uint16_t* dst = Y + (size_t)r * N + c0;
   const uint16_t o[4] = {__half_as_ushort(__float2half_rn(0.25f * y[0])), __half_as_ushort(__float2half_rn(0.25f * y[1])),
                          __half_as_ushort(__float2half_rn(0.25f * y[2])), __half_as_ushort(__float2half_rn(0.25f * y[3]))};
@@ -166,23 +188,38 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
 
 }  // namespace
 
-hipError_t launch_gemm_small(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M,
-                             int N, int K, uint16_t* Y, hipStream_t stream) {
+namespace {
+// Range plan: ranges of 4 groups while they fit one wave each; beyond 16 ranges, ranges of 6
+// (fewer waves that take a second range).  Measured on 16-token batches (event-timed): 16 x
+// 11008 x 4096 (85 INT4 groups) 11.3 -> 10.7 us with ranges of 6; with 31 INT4 groups ranges of
+// 6 are slower (16 x 4096 x 11008: 11.1 -> 11.4 us), and ranges of 2 are slower everywhere.
+template <bool kAcc>
+hipError_t launch_small(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
+                        int K, uint16_t* Y, int32_t* acc, hipStream_t stream) {
   const int G = K / ATOM_GROUP;
-  // Ranges of 4 groups while they fit one wave each; beyond 16 ranges, ranges of 6 (fewer
-  // waves that take a second range).  Measured on 16-token batches (event-timed): 16 x 11008
-  // x 4096 (85 INT4 groups) 11.3 -> 10.7 us with ranges of 6; with 31 INT4 groups ranges of 6
-  // are slower (16 x 4096 x 11008: 11.1 -> 11.4 us), and ranges of 2 are slower everywhere.
   const bool wide = (G - 1 + 3) / 4 > kMaxWaves;
   const int maxg = wide ? 6 : 4;
   const int ranges = (G - 1 + maxg - 1) / maxg;
   const int waves = ranges < kMaxWaves ? ranges : kMaxWaves;
   const dim3 grid((N + kCols - 1) / kCols), block(64 * waves);
   if (wide)
-    hipLaunchKernelGGL(gemm_w4a4_small_kernel<6>, grid, block, 0, stream, Xq, sx, Wq, sw, M, N, K, ranges, Y);
+    hipLaunchKernelGGL((gemm_w4a4_small_kernel<6, kAcc>), grid, block, 0, stream, Xq, sx, Wq, sw, M, N, K, ranges, Y,
+                       acc);
   else
-    hipLaunchKernelGGL(gemm_w4a4_small_kernel<4>, grid, block, 0, stream, Xq, sx, Wq, sw, M, N, K, ranges, Y);
+    hipLaunchKernelGGL((gemm_w4a4_small_kernel<4, kAcc>), grid, block, 0, stream, Xq, sx, Wq, sw, M, N, K, ranges, Y,
+                       acc);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_small(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M,
+                             int N, int K, uint16_t* Y, hipStream_t stream) {
+  return launch_small<false>(Xq, sx, Wq, sw, M, N, K, Y, nullptr, stream);
+}
+
+hipError_t launch_gemm_small_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K, int32_t* acc,
+                                       hipStream_t stream) {
+  return launch_small<true>(Xq, nullptr, Wq, nullptr, M, N, K, nullptr, acc, stream);
 }
 
 }  // namespace atom

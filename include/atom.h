@@ -158,7 +158,8 @@ int atom_gemm_ws(const void *Xq, const void *sx, const void *Wq, const void *sw,
 
 /*
  * Per-group integer accumulators (verification aid): acc[g, m, n] = acc_g[m,n] as defined
- * for atom_gemm, computed by the same main loop.  acc is int32 [G, M, N] (output,
+ * for atom_gemm, computed by the main loop of the kernel atom_gemm runs for this shape (the
+ * few-rows kernel for M <= 16, the tiled kernel otherwise).  acc is int32 [G, M, N] (output,
  * G*M*N*4 bytes).
  */
 int atom_gemm_group_acc(const void *Xq, const void *Wq, int32_t M, int32_t N, int32_t K,

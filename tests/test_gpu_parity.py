@@ -158,12 +158,35 @@ def test_group_acc_bitexact(key):
     np.testing.assert_array_equal(acc, O.group_acc(qx, qw))
 
 
+@pytest.mark.parametrize("key,extra_rows,ncols", [("B", 256, 384), ("C", 0, 256)])
+def test_group_acc_bitexact_llama_shapes(key, extra_rows, ncols):
+    """Per-group accumulators bit-exact on the real packed operands of the Llama-7B MLP shapes,
+    with at least 1152 activation-side rows so the banded tile order (bands of 8 tile rows of
+    128) runs past its first band: C with all 2048 token rows (two bands), B with its 1024 token
+    rows followed by 256 of its packed weight rows (a partial second band of 2 tile rows)."""
+    w, x, wt, perm = workload(key)
+    _say(f"[acc] {key} llama shape, {w.M + extra_rows} x {ncols}")
+    Pd = dev(perm)
+    Xq, _ = bq.atom_quantize_act(dev(x), Pd)
+    Wq, _ = bq.atom_pack_weights(dev(wt), Pd)
+    A = torch.cat([Xq, Wq[:extra_rows]]).contiguous() if extra_rows else Xq
+    Bm = Wq[:ncols].contiguous()
+    acc = host(bq.atom_gemm_group_acc(A, Bm, w.K))
+    qx, _ = O.quantize_rows(x, perm)
+    qw, _ = O.quantize_rows(wt[:max(ncols, extra_rows)], perm)
+    qa = np.concatenate([qx, qw[:extra_rows]]) if extra_rows else qx
+    ref = O.group_acc(qa, qw[:ncols])
+    assert acc.shape == ref.shape and acc.shape[1] >= 1152
+    np.testing.assert_array_equal(acc, ref)
+
+
 @pytest.mark.parametrize("M,N", [(15, 40), (45, 150)])
 def test_oracle_packed_units_every_code_in_every_field(M, N):
     """The GEMMs read packed rows written by the oracle's packer (not by the GPU quantize):
     every INT4 code value sits in every field position of a 16-code unit, the folded third
-    word included, and the INT8 group spans [-127, 127].  Group accumulators bit-exact; Y
-    within tolerance on the few-rows kernel (M <= 16) and the tiled kernel."""
+    word included, and the INT8 group spans [-127, 127].  Group accumulators bit-exact and Y
+    within tolerance, on the few-rows kernel (M = 15) and on the tiled kernel (M = 45):
+    atom_gemm_group_acc runs the kernel atom_gemm runs for the shape."""
     K = 1152
     klo, G = K - O.OUTLIERS, K // O.GROUP
     _say(f"[units] M={M} N={N} K={K}")
@@ -213,6 +236,16 @@ def test_gemm_llama70b_sampled():
     qx, sxr = O.quantize_rows(x[rows], perm)
     qw, swr = O.quantize_rows(wt[cols], perm)
     assert_y_close(host(Y)[np.ix_(rows, cols)], O.gemm_ref(qx, sxr, qw, swr), "D")
+    # per-group accumulators bit-exact on a seeded slice: 1152 token rows (two tile-row bands)
+    # against 384 weight rows, gathered from the packed operands of the full-size pack
+    arows = np.sort(rng.choice(w.M, 1152, replace=False))
+    acols = np.sort(rng.choice(w.N, 384, replace=False))
+    ti = lambda a: torch.from_numpy(a).cuda()
+    acc = host(bq.atom_gemm_group_acc(Xq.index_select(0, ti(arows)).contiguous(),
+                                      Wq.index_select(0, ti(acols)).contiguous(), w.K))
+    qxa, _ = O.quantize_rows(x[arows], perm)
+    qwa, _ = O.quantize_rows(wt[acols], perm)
+    np.testing.assert_array_equal(acc, O.group_acc(qxa, qwa))
 
 
 # --------------------------------------------------------------------------- ragged / edge shapes
