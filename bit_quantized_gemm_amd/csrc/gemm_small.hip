@@ -67,6 +67,13 @@ __device__ __forceinline__ h4 scale_operand(uint16_t v) {
 
 constexpr int kMaxWaves = 16;                // waves (K ranges in flight) per workgroup
 
+// The kAcc stores sit under a per-lane branch (token rows past M store nothing).  Left alone,
+// the compiler sinks the operand decode and the MFMA that feed a store into that branch; the
+// decode then runs with those lanes switched off, and the matrix core, which reads every lane,
+// multiplies stale operand registers for their rows.  An empty asm statement that takes the
+// result as an in/out operand pins the MFMA (and everything it reads) before the branch.
+__device__ __forceinline__ void keep_in_all_lanes(v4f& v) { asm volatile("" : "+v"(v)); }
+
 // blockIdx.x: column block (columns n0 = 16 blockIdx.x ..); wave w handles K ranges w, w + waves, ...
 // kAcc = true: write each group's exact integer sums to acc_out [G, M, N] instead of Y (the
 // same loads, decode and MFMAs; no scales are read).
@@ -140,7 +147,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
       // cbsz = blgp = 2: both operands fp6 e2m3
       const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{}, 2, 2, 0, kScaleE8M0, 0, kScaleE8M0);
       if (kAcc) {
-        if (i < ng) store_acc(ga + i, acc);
+        v4f a4 = acc;
+        keep_in_all_lanes(a4);
+        if (i < ng) store_acc(ga + i, a4);
         continue;
       }
       const uint16_t ws = i < ng ? wsc[i] : (uint16_t)0;
@@ -152,7 +161,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const u
       v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8[0], x8[0], v4i{}, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8[1], x8[1], acc, 0, 0, 0);
       if (kAcc) {
-        if (last) store_acc(G - 1, v4f{(float)acc[0], (float)acc[1], (float)acc[2], (float)acc[3]});
+        v4f a4 = v4f{(float)acc[0], (float)acc[1], (float)acc[2], (float)acc[3]};
+        keep_in_all_lanes(a4);
+        if (last) store_acc(G - 1, a4);
         continue;
       }
       const uint16_t ws = last ? wsc8 : (uint16_t)0;
