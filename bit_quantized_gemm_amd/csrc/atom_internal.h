@@ -32,9 +32,12 @@ hipError_t launch_row_quantize(const uint16_t* X, const int32_t* perm, int rows,
 // tiles go to caller scratch and are added by a second kernel.  rem == 0: no split.  The
 // kernel takes any mix; gemm_plan returns either no split or every tile split.
 // small != 0 instead selects the few-rows kernel (gemm_small.hip), which needs no scratch.
+// tile64 != 0 instead runs whole 64 x 64 output tiles (two waves of 32 x 64 each), for grids
+// that have too few 128 x 128 tiles to fill the GPU but enough 64 x 64 ones: no split, no scratch.
 struct GemmPlan {
   int full, rem, splits;
   int small;
+  int tile64;
 };
 // Few-rows kernel: at most kSmallMaxM token rows.
 constexpr int kSmallMaxM = 16;

@@ -115,11 +115,30 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Compile-time ring position of a stage buffer.
-template <int P>
+// Compile-time ring position of a stage buffer in a ring of NB buffers.
+template <int P, int NB>
 struct Ring {
-  static constexpr int kCur = P, kNext = (P + 1) % 3;
+  static constexpr int kCur = P, kNext = (P + 1) % NB, kAfterNext = (P + 2) % NB;
 };
+
+// f(Ring<P, NB>, s + P) for P = 0 .. NB-1: one turn of the ring, every buffer index a constant.
+template <int P, int NB, class F>
+__device__ __forceinline__ void ring_turn(F& f, int s) {
+  if constexpr (P < NB) {
+    f(Ring<P, NB>{}, s + P);
+    ring_turn<P + 1, NB>(f, s);
+  }
+}
+// The same for the groups s .. gb-1 left after the whole turns (fewer than NB).
+template <int P, int NB, class F>
+__device__ __forceinline__ void ring_tail(F& f, int s, int gb) {
+  if constexpr (P < NB - 1) {
+    if (s + P < gb) {
+      f(Ring<P, NB>{}, s + P);
+      ring_tail<P + 1, NB>(f, s, gb);
+    }
+  }
+}
 
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
@@ -182,20 +201,43 @@ __device__ __forceinline__ uint16_t load_scale(const StageAddr<NDMA>& ad, int s,
 // last `rem` tiles are divided among `splits` pieces (the last piece also takes the INT8
 // group), each writing its fp32 tile sum, still carrying the factor 2 of the scale
 // products, tile-major to part[(piece split * rem + tile - full) * BM * BN].
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool kAcc>
+// NBUF stage buffers (3 .. 8) form the ring: NBUF - 1 stages of copies are in flight ahead of
+// the group being multiplied.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NBUF, bool kAcc>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(kAcc ? 1 : 2))) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx, const uint8_t* __restrict__ Wq,
     const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out,
     int full, int rem, int splits, float* __restrict__ part) {
   using T = Tile<BM, BN, WAVES_M, WAVES_N>;
-  // Three stage buffers, each its own object: the compiler then knows that a copy into one
-  // does not write what is read from another, and waits only where a buffer is really shared.
-  __shared__ __attribute__((aligned(16))) uint8_t la0[BM * kLdsRow], la1[BM * kLdsRow], la2[BM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint8_t lb0[BN * kLdsRow], lb1[BN * kLdsRow], lb2[BN * kLdsRow];
-  __shared__ __attribute__((aligned(16))) h4 ls0[BM + BN], ls1[BM + BN], ls2[BM + BN];   // sx rows, then sw
-  auto LA = [&](int p) -> uint8_t* { return p == 0 ? la0 : p == 1 ? la1 : la2; };
-  auto LB = [&](int p) -> uint8_t* { return p == 0 ? lb0 : p == 1 ? lb1 : lb2; };
-  auto LS = [&](int p) -> h4* { return p == 0 ? ls0 : p == 1 ? ls1 : ls2; };
+  static_assert(NBUF >= 3 && NBUF <= 8, "ring of 3 to 8 stage buffers");
+  // The stage buffers, each its own object: the compiler then knows that a copy into one does
+  // not write what is read from another, and waits only where a buffer is really shared.
+  // Buffers past NBUF are never referenced and take no LDS.
+  __shared__ __attribute__((aligned(16))) uint8_t la0[BM * kLdsRow], la1[BM * kLdsRow], la2[BM * kLdsRow],
+      la3[BM * kLdsRow], la4[BM * kLdsRow], la5[BM * kLdsRow], la6[BM * kLdsRow], la7[BM * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint8_t lb0[BN * kLdsRow], lb1[BN * kLdsRow], lb2[BN * kLdsRow],
+      lb3[BN * kLdsRow], lb4[BN * kLdsRow], lb5[BN * kLdsRow], lb6[BN * kLdsRow], lb7[BN * kLdsRow];
+  // sx rows, then sw columns, each as a ready scale operand
+  __shared__ __attribute__((aligned(16))) h4 ls0[BM + BN], ls1[BM + BN], ls2[BM + BN], ls3[BM + BN], ls4[BM + BN],
+      ls5[BM + BN], ls6[BM + BN], ls7[BM + BN];
+  auto LA = [&](int p) -> uint8_t* {
+    switch (p) {
+      case 0: return la0; case 1: return la1; case 2: return la2; case 3: return la3;
+      case 4: return la4; case 5: return la5; case 6: return la6; default: return la7;
+    }
+  };
+  auto LB = [&](int p) -> uint8_t* {
+    switch (p) {
+      case 0: return lb0; case 1: return lb1; case 2: return lb2; case 3: return lb3;
+      case 4: return lb4; case 5: return lb5; case 6: return lb6; default: return lb7;
+    }
+  };
+  auto LS = [&](int p) -> h4* {
+    switch (p) {
+      case 0: return ls0; case 1: return ls1; case 2: return ls2; case 3: return ls3;
+      case 4: return ls4; case 5: return ls5; case 6: return ls6; default: return ls7;
+    }
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -325,38 +367,34 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
     for (int j = 0; j < T::kTN; ++j) pb[j] = read_b(lb, j);
   };
 
-  // Stage ring.  Stage t (t = ga, ga+1, ...) lives in LDS buffer (t - ga) % 3.  While group s
+  // Stage ring.  Stage t (t = ga, ga+1, ...) lives in LDS buffer (t - ga) % NBUF.  While group s
   // is multiplied, its packed operands and scales are in registers; stage s+1 has landed and
-  // each wave reads it into the registers that group s's decode has just freed; the copies
-  // of stage s+2 (issued at the start of group s-1) and stage s+3 (issued at the start of
-  // group s, into the buffer stage s came from) are in flight.  The one barrier per group
-  // comes after this wave's copy of stage s+2 has landed and its reads of stage s+1 have
-  // completed: after it stage s+2 is visible to all and the buffer of stage s+1 may be
-  // refilled.  Scales take the same ring: each thread's scale of stage t is loaded into
-  // `sreg` during group t-4 and written to LDS at the start of group t-3.
+  // each wave reads it into the registers that group s's decode has just freed; the copies of
+  // stages s+2 .. s+NBUF are in flight (stage s+NBUF issued at the start of group s, into the
+  // buffer stage s came from).  The one barrier per group comes after this wave's copy of stage
+  // s+2 has landed and its reads of stage s+1 have completed: after it stage s+2 is visible to
+  // all and the buffer of stage s+1 may be refilled.  Scales travel with their stage: the scale
+  // of stage t is loaded into sreg[(t - ga) % NBUF] just before stage t's copy is issued, and
+  // written to LDS at the start of group t-2 (its buffer's previous stage was read during group
+  // t-NBUF-1; loads complete in order, so waiting for that scale waits only for the copies of
+  // stages up to t-1, which the ring needs by then anyway).
   constexpr int kPerStage = 2 * T::kDma + (kAcc ? 0 : 1);   // vector-memory operations per stage
-  uint16_t sreg = 0;
-  {
-    uint16_t s0 = 0, s1 = 0, s2 = 0;
-    if (!kAcc) {
-      s0 = load_scale(ad, ga, G, M, N);
-      s1 = load_scale(ad, ga + 1, G, M, N);
-      s2 = load_scale(ad, ga + 2, G, M, N);
-    }
+  constexpr int kInFlight = (NBUF - 2) * kPerStage;         // at most this many once stage s+2 landed
+  static_assert(kInFlight <= 63, "vmcnt range");
+  uint16_t sreg[NBUF];
+#pragma unroll
+  for (int q = 0; q < NBUF; ++q) {
+    sreg[q] = kAcc ? (uint16_t)0 : load_scale(ad, ga + q, G, M, N);
     __builtin_amdgcn_sched_barrier(0);
-    dma_stage(ad, la0, lb0, ga);
-    dma_stage(ad, la1, lb1, min(ga + 1, G));
-    dma_stage(ad, la2, lb2, min(ga + 2, G));
+    dma_stage(ad, LA(q), LB(q), min(ga + q, G));
     __builtin_amdgcn_sched_barrier(0);
-    if (!kAcc) {
-      sreg = load_scale(ad, ga + 3, G, M, N);
-      ls0[tid] = scale_operand(s0);
-      ls1[tid] = scale_operand(s1);
-      ls2[tid] = scale_operand(s2);
-    }
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kPerStage));   // stages ga and ga+1 have landed
-    wg_barrier();
   }
+  if (!kAcc) {
+    LS(0)[tid] = scale_operand(sreg[0]);
+    LS(1)[tid] = scale_operand(sreg[1]);
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kInFlight));   // stages ga and ga+1 have landed
+  wg_barrier();
   v8i pa[T::kTM], pb[T::kTN];
   h4 sa[T::kTM], sb[T::kTN];
   if (!kAcc) read_scales(ls0, sa, sb);
@@ -373,15 +411,14 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   // in fp32) and its scale product are complete when they are used, and no more than two
   // tiles' sums and scale products are live at a time.  The scheduling fences keep this order.
   static_assert(T::kTN == 2, "tile rows are processed as pairs of 32x32 tiles");
-  auto int4_group = [&](auto ring, int s) {
-    constexpr int p = decltype(ring)::kCur, pn = decltype(ring)::kNext;
+  auto int4_group = [&](auto ring, int s) __attribute__((always_inline)) {
+    constexpr int p = decltype(ring)::kCur, pn = decltype(ring)::kNext, p2 = decltype(ring)::kAfterNext;
+    // scale of stage s+2 into its buffer (read during group s+1)
+    if (!kAcc) LS(p2)[tid] = scale_operand(sreg[p2]);
     // refill buffer p (stage s was read during group s-1, before the last barrier)
-    if (!kAcc) {
-      LS(p)[tid] = scale_operand(sreg);
-      sreg = load_scale(ad, s + 4, G, M, N);
-    }
+    if (!kAcc) sreg[p] = load_scale(ad, s + NBUF, G, M, N);
     __builtin_amdgcn_sched_barrier(0);
-    dma_stage(ad, LA(p), LB(p), min(s + 3, G));               // past the row end: unused
+    dma_stage(ad, LA(p), LB(p), min(s + NBUF, G));            // past the row end: unused
     __builtin_amdgcn_sched_barrier(0);
     v16f acc0, sp0, acc1, sp1;                                 // tiles (i, 0) and (i, 1)
     v8i b0[2], b1[2];                                          // fp6 operands of the B columns
@@ -411,7 +448,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
       __builtin_amdgcn_sched_barrier(0);
     }
     apply(T::kTM - 1, 1, acc1, sp1, s);
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kPerStage));   // own copy of stage s+2 landed, reads done
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kInFlight));   // own copy of stage s+2 landed, reads done
     wg_barrier();
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i) sa[i] = san[i];
@@ -420,13 +457,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   };
   {
     int s = ga;
-    for (; s + 3 <= gb; s += 3) {
-      int4_group(Ring<0>{}, s);
-      int4_group(Ring<1>{}, s + 1);
-      int4_group(Ring<2>{}, s + 2);
-    }
-    if (s < gb) int4_group(Ring<0>{}, s++);
-    if (s < gb) int4_group(Ring<1>{}, s++);
+    for (; s + NBUF <= gb; s += NBUF) ring_turn<0, NBUF>(int4_group, s);
+    ring_tail<0, NBUF>(int4_group, s, gb);
   }
 
   // INT8 outlier group: stage G-1 (its packed operands are in pa / pb, the group's scales in
@@ -442,10 +474,10 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
         acc[i][j] = mma_i8(lo(pa[i]), lo(pb[j]), v16i{});
         acc[i][j] = mma_i8(hi(pa[i]), hi(pb[j]), acc[i][j]);
       }
-    const int pg = (G - ga) % 3;
-    if (pg == 0) read_packed(la0, lb0, pa, pb);
-    else if (pg == 1) read_packed(la1, lb1, pa, pb);
-    else read_packed(la2, lb2, pa, pb);
+    const int pg = (G - ga) % NBUF;                 // stage G's buffer
+#pragma unroll
+    for (int q = 0; q < NBUF; ++q)
+      if (pg == q) read_packed(LA(q), LB(q), pa, pb);
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i)
 #pragma unroll
@@ -513,7 +545,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
 }
 
 // 128 x 128 workgroup tile, 2 x 2 waves of 64 x 64 (2 x 2 MFMA tiles of 32 x 32 each).
-constexpr int kBM = 128, kBN = 128, kWavesM = 2, kWavesN = 2;
+constexpr int kBM = 128, kBN = 128, kWavesM = 2, kWavesN = 2, kRing = 3;
 // Split-K.  Grids of fewer than kSplitMinTiles tiles split every tile, aiming at about one
 // workgroup per compute unit; a piece keeps at least kSplitMinGroups INT4 groups.  Larger
 // grids are not split, not even a last partial round of tiles: with every compute unit busy
@@ -522,6 +554,13 @@ constexpr int kBM = 128, kBN = 128, kWavesM = 2, kWavesN = 2;
 // 1024 x 4096 x 11008 with its last 176 of 688 tiles split in two spans the same time, and
 // 600 x 2048 x 15300 with 88 of 600 split three ways is slower).
 constexpr int kSplitMinTiles = 128, kSplitTargetBlocks = 256, kSplitMinGroups = 4, kSplitMax = 8;
+// 64 x 64 output tiles, two waves of 32 x 64 (one 32 x 32 MFMA tile row, two columns): for grids
+// with fewer than kSplitMinTiles tiles of 128 x 128 but at least k64MinTiles of 64 x 64, whole
+// small tiles replace split-K (no partial sums, no second kernel, no scratch).  Measured on
+// 256 x 4096 x 4096 (kernel trace): 16.0 us against 19.9 us for four split-K pieces of 128 x 128
+// plus 4.4 us for their finalize kernel.  A deeper ring does not help these tiles (event-timed:
+// 3 or 4 buffers 18.3 us, 6 buffers 21.5 us, 8 buffers 22.2 us), so they keep three.
+constexpr int k64 = 64, k64WavesM = 2, k64WavesN = 1, k64Ring = 3, k64MinTiles = 192;
 
 // Y of the split tiles = fp16(0.5 * sum over pieces of the partial tiles), pieces added in
 // order.  blockIdx.y = split tile (tile full + blockIdx.y in tile order); four consecutive
@@ -563,29 +602,39 @@ __global__ __launch_bounds__(256) void gemm_splitk_finish_kernel(const float* __
 }  // namespace
 
 GemmPlan gemm_plan(int M, int N, int K) {
-  if (M <= kSmallMaxM) return GemmPlan{0, 0, 1, 1};
+  if (M <= kSmallMaxM) return GemmPlan{0, 0, 1, 1, 0};
+  const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  const int tiles64 = ((M + k64 - 1) / k64) * ((N + k64 - 1) / k64);
+  if (tiles < kSplitMinTiles && tiles64 >= k64MinTiles) return GemmPlan{tiles64, 0, 1, 0, 1};
   return gemm_plan_tiled(M, N, K);
 }
 
 GemmPlan gemm_plan_tiled(int M, int N, int K) {
   const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   const int G = K / ATOM_GROUP;
-  if (tiles >= kSplitMinTiles) return GemmPlan{tiles, 0, 1, 0};
+  if (tiles >= kSplitMinTiles) return GemmPlan{tiles, 0, 1, 0, 0};
   const int s = min(min((kSplitTargetBlocks + tiles - 1) / tiles, (G - 1) / kSplitMinGroups), kSplitMax);
-  return s < 2 ? GemmPlan{tiles, 0, 1, 0} : GemmPlan{0, tiles, s, 0};
+  return s < 2 ? GemmPlan{tiles, 0, 1, 0, 0} : GemmPlan{0, tiles, s, 0, 0};
 }
 
 int64_t gemm_workspace_bytes(const GemmPlan& plan) {
-  if (plan.small) return 0;
+  if (plan.small || plan.tile64) return 0;
   return plan.rem > 0 ? (int64_t)plan.rem * plan.splits * kBM * kBN * (int64_t)sizeof(float) : 0;
 }
 
 hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
                        int K, uint16_t* Y, float* part, const GemmPlan& plan, hipStream_t stream) {
   if (plan.small) return launch_gemm_small(Xq, sx, Wq, sw, M, N, K, Y, stream);
+  if (plan.tile64) {
+    if (plan.rem != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_w4a4_kernel<k64, k64, k64WavesM, k64WavesN, k64Ring, false>), dim3(plan.full),
+                       dim3(k64WavesM * k64WavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr,
+                       plan.full, 0, 1, (float*)nullptr);
+    return hipGetLastError();
+  }
   if (plan.rem > 0 && (plan.splits < 2 || plan.splits > kSplitMax)) return hipErrorInvalidValue;
   const int blocks = plan.full + plan.rem * plan.splits;
-  hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, false>), dim3(blocks),
+  hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, kRing, false>), dim3(blocks),
                      dim3(kWavesM * kWavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr,
                      plan.full, plan.rem, plan.splits, part);
   if (plan.rem > 0) return launch_splitk_finish(part, plan, M, N, Y, stream);
@@ -607,9 +656,16 @@ hipError_t launch_splitk_finish(const float* part, const GemmPlan& plan, int M, 
 
 hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K, int32_t* acc,
                                  hipStream_t stream) {
-  if (gemm_plan(M, N, K).small) return launch_gemm_small_group_acc(Xq, Wq, M, N, K, acc, stream);
+  const GemmPlan plan = gemm_plan(M, N, K);
+  if (plan.small) return launch_gemm_small_group_acc(Xq, Wq, M, N, K, acc, stream);
+  if (plan.tile64) {
+    hipLaunchKernelGGL((gemm_w4a4_kernel<k64, k64, k64WavesM, k64WavesN, k64Ring, true>), dim3(plan.full),
+                       dim3(k64WavesM * k64WavesN * 64), 0, stream, Xq, (const uint16_t*)nullptr, Wq,
+                       (const uint16_t*)nullptr, M, N, K, (uint16_t*)nullptr, acc, plan.full, 0, 1, (float*)nullptr);
+    return hipGetLastError();
+  }
   const dim3 grid(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM));
-  hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, true>), grid, dim3(kWavesM * kWavesN * 64), 0,
+  hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, kRing, true>), grid, dim3(kWavesM * kWavesN * 64), 0,
                      stream, Xq, (const uint16_t*)nullptr, Wq, (const uint16_t*)nullptr, M, N, K,
                      (uint16_t*)nullptr, acc, (int)grid.x, 0, 1, (float*)nullptr);
   return hipGetLastError();

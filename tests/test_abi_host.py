@@ -185,14 +185,16 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 def test_gemm_workspace_query(lib):
     # fp32 partial tiles of 128 x 128, tile-major: bytes = split tiles x pieces x 64 KiB
     T = 128 * 128 * 4
-    # 256 x 4096 output = 2 x 32 tiles: every tile split four ways
-    assert bq.atom_gemm_workspace_bytes(256, 4096, 4096) == 64 * 4 * T
+    # 256 x 4096 output = 2 x 32 tiles of 128 x 128 but 4 x 64 of 64 x 64: whole small tiles, no scratch
+    assert bq.atom_gemm_workspace_bytes(256, 4096, 4096) == 0
+    # 33 x 8448: 66 tiles of 128 x 128, 132 of 64 x 64 (too few): every 128 x 128 tile split four ways
+    assert bq.atom_gemm_workspace_bytes(33, 8448, 4096) == 66 * 4 * T
     assert bq.atom_gemm_workspace_bytes(64, 128, 4096) == 1 * 7 * T       # capped by 31 INT4 groups / 4
     # M <= 16: the few-rows kernel reduces its K ranges inside the workgroup: no scratch
     for M, N, K in [(1, 130, 1152), (1, 4096, 4096), (16, 4096, 11008), (3, 131, 2048), (16, 16, 32768)]:
         assert bq.atom_gemm_workspace_bytes(M, N, K) == 0
     assert bq.atom_gemm_workspace_bytes(17, 128, 4096) == 1 * 7 * T        # 17 rows: 128 x 128 tiles, split-K
-    assert bq.atom_gemm_workspace_bytes(127 * 128, 128, 256 * 128) == 127 * 3 * T   # ceil(256 / 127) = 3
+    assert bq.atom_gemm_workspace_bytes(90 * 128, 64, 4096) == 90 * 3 * T   # ceil(256 / 90) = 3; 180 small tiles
     # 128 tiles or more, or too few groups to divide: no scratch
     assert bq.atom_gemm_workspace_bytes(128 * 128, 128, 4096) == 0
     assert bq.atom_gemm_workspace_bytes(2048, 4096, 11008) == 0

@@ -319,9 +319,8 @@ def test_deterministic_and_side_stream():
 
 
 # --------------------------------------------------------------------------- split-K (atom_gemm_ws)
-# pieces per split tile: 7, 3, 2, 4 (the Llama-7B attention projection), 5, 6, 8; every piece count
-# has its own finalize instance
-SPLIT = [(64, 128, 4096), (200, 300, 2048), (17, 130, 1152), (256, 4096, 4096), (17, 64, 3072), (40, 200, 3456),
+# pieces per split tile: 7, 3, 2, 4, 5, 6, 8; every piece count has its own finalize instance
+SPLIT = [(64, 128, 4096), (200, 300, 2048), (17, 130, 1152), (33, 8448, 4096), (17, 64, 3072), (40, 200, 3456),
          (33, 250, 4352)]
 
 
@@ -343,6 +342,30 @@ def test_gemm_ws_split_matches_oracle(M, N, K):
     assert_y_close(Y, O.gemm_ref(qx, sxr, qw, swr), f"split {M}x{N}x{K}")
     Y2 = host(bq.atom_gemm_ws(Xq, sx, Wq, sw, K, ws))          # deterministic: splits summed in order
     np.testing.assert_array_equal(Y.view(np.uint16), Y2.view(np.uint16))
+
+
+# Grids with few 128 x 128 tiles but at least 192 of 64 x 64 run whole 64 x 64 tiles (no split,
+# no scratch): the Llama-7B attention projection, ragged edges, and group counts that leave a
+# partial turn of the eight-stage ring (K = 640: 4 INT4 groups, 4096: 31, 1152: 8, 11008: 85).
+TILE64 = [(256, 4096, 4096), (200, 4000, 640), (130, 5000, 1152), (100, 6100, 11008), (255, 3100, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", TILE64)
+def test_gemm_tile64_matches_oracle(M, N, K):
+    _say(f"[tile64] M={M} N={N} K={K}")
+    assert bq.atom_gemm_workspace_bytes(M, N, K) == 0
+    x, wt, _ = synth.make_linear(M, K, N, seed=5 * M + N + K)
+    perm = np.random.default_rng(K + 7).permutation(K).astype(np.int32)
+    Xq, sx = bq.atom_quantize_act(dev(x), dev(perm))
+    Wq, sw = bq.atom_pack_weights(dev(wt), dev(perm))
+    Y = host(bq.atom_gemm(Xq, sx, Wq, sw, K))
+    qx, sxr = O.quantize_rows(x, perm)
+    qw, swr = O.quantize_rows(wt, perm)
+    assert_y_close(Y, O.gemm_ref(qx, sxr, qw, swr), f"tile64 {M}x{N}x{K}")
+    if N * M * (K // 128) <= 40_000_000:
+        np.testing.assert_array_equal(host(bq.atom_gemm_group_acc(Xq, Wq, K)), O.group_acc(qx, qw))
+    for y2 in (bq.atom_gemm(Xq, sx, Wq, sw, K), bq.atom_gemm_ws(Xq, sx, Wq, sw, K, None)):
+        np.testing.assert_array_equal(Y.view(np.uint16), host(y2).view(np.uint16))
 
 
 def test_gemm_ws_without_enough_scratch_is_atom_gemm():
@@ -387,10 +410,11 @@ def test_gemm_small_m_matches_oracle(M, N, K):
 # --------------------------------------------------------------------------- HIP graph capture
 def test_graph_capture_replays_match_eager():
     """The library allocates and synchronizes nothing, so quantize + GEMM can be captured in a
-    HIP graph.  Three shapes cover the three GEMM paths (split-K with its finalize kernel, whole
-    128 x 128 tiles, few rows); the graph is replayed several times with unrelated eager work
-    and new inputs in between, and every replay must equal the eager result bit for bit."""
-    cases = [(256, 4096, 4096), (1024, 2048, 1024), (16, 2000, 11008)]
+    HIP graph.  Four shapes cover the four GEMM paths (whole 64 x 64 tiles, split-K with its
+    finalize kernel, whole 128 x 128 tiles, few rows); the graph is replayed several times with
+    unrelated eager work and new inputs in between, and every replay must equal the eager
+    result bit for bit."""
+    cases = [(256, 4096, 4096), (64, 2048, 4096), (1024, 2048, 1024), (16, 2000, 11008)]
     st = torch.cuda.Stream()
     bufs = []
     for i, (M, N, K) in enumerate(cases):
