@@ -332,6 +332,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="resident input copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="rows per shape in the CPU oracle sample (2048: every row)")
+    ap.add_argument("--path", default="separate", choices=["separate", "fused"],
+                    help="separate: atom_quantize_act then atom_gemm_ws; fused: atom_linear (one persistent "
+                         "launch where the shape allows)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (steps times), to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -367,6 +370,10 @@ def main():
 
     # ---------------------------------------------------------------- offline: inputs, perm, weight pack
     w4a8 = args.workload == "w4a8"
+    fused = args.path == "fused"
+    if fused and w4a8:
+        print("--path fused applies to the W4A4 path only", file=sys.stderr)
+        sys.exit(2)
     sets = []
     for key in keys:
         w = synth.get(key)
@@ -388,7 +395,10 @@ def main():
         # split-K scratch for shapes with few output tiles (allocated once, outside the timed region)
         need = (bq.atom_gemm_w4a8_workspace_bytes if w4a8 else bq.atom_gemm_workspace_bytes)(w.M, w.N, w.K)
         ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
-        sets.append(dict(key=key, w=w, perm=perm, copies=copies, ws=ws))
+        # atom_linear's workspace (queue and counters; zero before the first call, kept zero)
+        lws = torch.zeros(bq.atom_linear_workspace_bytes(w.M, w.N, w.K), dtype=torch.uint8, device=dev) \
+            if fused else None
+        sets.append(dict(key=key, w=w, perm=perm, copies=copies, ws=ws, lws=lws))
         log(f"[setup] {key} {w.name} ready ({R} copies)")
     torch.cuda.synchronize()
 
@@ -400,6 +410,14 @@ def main():
             w = s["w"]
             if evs is not None:
                 evs[si][0].record(stream)
+            if fused:
+                if evs is not None:
+                    evs[si][1].record(stream)
+                bq.atom_linear(c["X"], s["perm"], c["Wq"], c["sw"], s["lws"], Xq=c["Xq"], sx=c["sx"], Y=c["Y"],
+                               stream=stream)
+                if evs is not None:
+                    evs[si][2].record(stream)
+                continue
             if w4a8:
                 bq.atom_quantize_act_a8(c["X"], s["perm"], Xq=c["Xq"], sx=c["sx"], stream=stream)
             else:
@@ -515,6 +533,8 @@ def main():
             "weights": "pre-packed INT4 + INT8 outlier group" + (" (offset-binary nibbles)" if w4a8 else ""),
             "activations": "INT8 in every group" if w4a8 else "INT4 + INT8 outlier group",
             "rotating_input_copies": R,
+            "path": ("atom_linear: quantize and GEMM in one launch where the shape allows" if fused else
+                     "atom_quantize_act then atom_gemm_ws"),
         },
         "roofline": {
             # every W4A8 group runs on the int8 matrix cores

@@ -15,6 +15,8 @@ The function names are the C entry points:
 * ``atom_gemm_group_acc(Xq, Wq, K)``      -> acc int32 [G, M, N]   (verification aid)
 * W4A8 variant: ``atom_quantize_act_a8(X, perm)`` -> (Xq u8 [M, K], sx), ``atom_pack_weights_w4a8(W, perm)``
   -> (Wq u8 [N, RB], sw), ``atom_gemm_w4a8(Xq, sx, Wq, sw, K)`` -> Y, ``atom_gemm_w4a8_group_acc(Xq, Wq, K)``
+* ``atom_linear(X, perm, Wq, sw, workspace)`` -> (Y, Xq, sx): quantize + GEMM, one persistent launch
+  where the shape allows (``atom_linear_workspace_bytes(M, N, K)``; the workspace starts zeroed)
 * ``atom_row_bytes(K)``, ``atom_num_groups(K)``, ``atom_strerror(status)``
 """
 from __future__ import annotations
@@ -28,6 +30,7 @@ __all__ = [
     "atom_pack_weights", "atom_quantize_act", "atom_gemm", "atom_gemm_workspace_bytes", "atom_gemm_ws",
     "atom_gemm_group_acc", "linear", "atom_quantize_act_a8", "atom_pack_weights_w4a8", "atom_gemm_w4a8",
     "atom_gemm_w4a8_group_acc", "atom_gemm_w4a8_workspace_bytes", "atom_gemm_w4a8_ws",
+    "atom_linear_workspace_bytes", "atom_linear", "linear_timed_out",
 ]
 
 GROUP = 128
@@ -40,6 +43,7 @@ EXPORTS = (
     "atom_pack_weights", "atom_quantize_act", "atom_gemm", "atom_gemm_workspace_bytes", "atom_gemm_ws",
     "atom_gemm_group_acc", "atom_quantize_act_a8", "atom_pack_weights_w4a8", "atom_gemm_w4a8",
     "atom_gemm_w4a8_group_acc", "atom_gemm_w4a8_workspace_bytes", "atom_gemm_w4a8_ws",
+    "atom_linear_workspace_bytes", "atom_linear",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -82,6 +86,8 @@ def load_library():
         "atom_gemm_w4a8_group_acc": (ctypes.c_int, [vp, vp, i32, i32, i32, vp, vp]),
         "atom_gemm_w4a8_workspace_bytes": (i64, [i32, i32, i32]),
         "atom_gemm_w4a8_ws": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp, i64, vp]),
+        "atom_linear_workspace_bytes": (i64, [i32, i32, i32]),
+        "atom_linear": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, i64, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -291,6 +297,45 @@ def linear(X, perm, Wq, sw, Y=None, stream=None, workspace=None):
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     return atom_gemm_ws(Xq, sx, Wq, sw, K, workspace if need else None, Y=Y, stream=stream)
+
+
+# --------------------------------------------------------------------------- fused forward
+def atom_linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    r = load_library().atom_linear_workspace_bytes(M, N, K)
+    if r < 0:
+        raise AtomError(f"atom_linear_workspace_bytes: {atom_strerror(-r)}")
+    return r
+
+
+def atom_linear(X, perm, Wq, sw, workspace, Xq=None, sx=None, Y=None, stream=None):
+    """Quantize X and run the grouped GEMM in one call (one persistent launch where the shape
+    allows).  ``workspace``: 1-D uint8 tensor of at least atom_linear_workspace_bytes(M, N, K)
+    bytes, zero before its first use (torch.zeros); calls leave it zero.  Returns (Y, Xq, sx)."""
+    torch = _torch()
+    M, K = _mat(X, "X")
+    N, _ = _mat(Wq, "Wq")
+    rb, g = _shape_k(K)
+    if Xq is None:
+        Xq = _empty((M, rb), torch.uint8, X)
+    if sx is None:
+        sx = _empty((g, M), torch.float16, X)
+    if Y is None:
+        Y = _empty((M, N), torch.float16, X)
+    if getattr(workspace, "dim", lambda: -1)() != 1:
+        raise AtomError("workspace must be a 1-D uint8 tensor")
+    ptrs = _ptrs((X, "X", torch.float16, None), (perm, "perm", torch.int32, (K,)), (Wq, "Wq", torch.uint8, (N, rb)),
+                 (sw, "sw", torch.float16, (g, N)), (Xq, "Xq", torch.uint8, (M, rb)),
+                 (sx, "sx", torch.float16, (g, M)), (Y, "Y", torch.float16, (M, N)),
+                 (workspace, "workspace", torch.uint8, None))
+    _check(load_library().atom_linear(ptrs[0], ptrs[1], ptrs[2], ptrs[3], M, N, K, ptrs[4], ptrs[5], ptrs[6], ptrs[7],
+                                      int(workspace.numel()), _stream(stream, X.device)), "atom_linear")
+    return Y, Xq, sx
+
+
+def linear_timed_out(workspace) -> bool:
+    """True if a bounded wait of an atom_linear call using this workspace gave up (int32 word 9;
+    read after the stream has completed)."""
+    return bool(workspace[36:40].view(_torch().int32).item())
 
 
 # --------------------------------------------------------------------------- W4A8 variant

@@ -167,6 +167,47 @@ int atom_gemm_group_acc(const void* Xq, const void* Wq, int32_t M, int32_t N, in
                                                 N, K, acc, static_cast<hipStream_t>(stream)));
 }
 
+// ---- fused runtime forward (activation quantize + GEMM)
+
+int64_t atom_linear_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (!valid_gemm(M, N, K)) return -(int64_t)ATOM_E_SHAPE;
+  return atom::linear_fused_workspace_bytes(M) + atom::gemm_workspace_bytes(atom::gemm_plan(M, N, K));
+}
+
+int atom_linear(const void* X, const int32_t* perm, const void* Wq, const void* sw, int32_t M, int32_t N, int32_t K,
+                void* Xq, void* sx, void* Y, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!X || !perm || !Wq || !sw || !Xq || !sx || !Y || !workspace) return ATOM_E_NULL;
+  if (!valid_gemm(M, N, K)) return ATOM_E_SHAPE;
+  const int64_t need = atom_linear_workspace_bytes(M, N, K);
+  if (workspace_bytes < need) return ATOM_E_SHAPE;
+  if (!aligned16(X) || !aligned16(perm) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Xq) || !aligned16(sx) ||
+      !aligned16(Y) || !aligned16(workspace))
+    return ATOM_E_ALIGN;
+  const uint64_t G = (uint64_t)K / ATOM_GROUP;
+  const uint64_t rb = (uint64_t)atom_row_bytes(K);
+  const Range in[4] = {range_of(X, (uint64_t)M * K * 2), range_of(perm, (uint64_t)K * 4),
+                       range_of(Wq, (uint64_t)N * rb), range_of(sw, G * N * 2)};
+  const Range out[4] = {range_of(Xq, (uint64_t)M * rb), range_of(sx, G * M * 2), range_of(Y, (uint64_t)M * N * 2),
+                        range_of(workspace, (uint64_t)need)};
+  if (int st = check_overlap(in, 4, out, 4)) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (atom::linear_fused_supported(M, N, K))
+    return hip_status(atom::launch_linear_fused(static_cast<const uint16_t*>(X), perm, static_cast<const uint8_t*>(Wq),
+                                                static_cast<const uint16_t*>(sw), M, N, K, static_cast<uint8_t*>(Xq),
+                                                static_cast<uint16_t*>(sx), static_cast<uint16_t*>(Y),
+                                                static_cast<int*>(workspace), s));
+  // two launches: the quantize, then the GEMM with the split-K part of the workspace
+  hipError_t e = atom::launch_row_quantize(static_cast<const uint16_t*>(X), perm, M, K, static_cast<uint8_t*>(Xq),
+                                           static_cast<uint16_t*>(sx), atom::kRowW4A4, s);
+  if (e != hipSuccess) return ATOM_E_HIP;
+  const atom::GemmPlan plan = atom::gemm_plan(M, N, K);
+  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + atom::linear_fused_workspace_bytes(M));
+  return hip_status(atom::launch_gemm(static_cast<const uint8_t*>(Xq), static_cast<const uint16_t*>(sx),
+                                      static_cast<const uint8_t*>(Wq), static_cast<const uint16_t*>(sw), M, N, K,
+                                      static_cast<uint16_t*>(Y), atom::gemm_workspace_bytes(plan) > 0 ? part : nullptr,
+                                      plan, s));
+}
+
 // ---- W4A8 variant
 
 int atom_quantize_act_a8(const void* X, const int32_t* perm, int32_t M, int32_t K, void* Xq, void* sx,

@@ -72,6 +72,13 @@ hipError_t launch_gemm_small(const uint8_t* Xq, const uint16_t* sx, const uint8_
 // kernel for M <= kSmallMaxM, the tiled kernel otherwise).
 hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K, int32_t* acc,
                                  hipStream_t stream);
+// Activation quantize + GEMM in one persistent launch (gemm.hip), for shapes whose GEMM runs whole
+// 128 x 128 tiles and K <= 12288 (linear_fused_supported).  ws: linear_fused_workspace_bytes(M)
+// bytes, zero before the first call and left zero by every call.
+bool linear_fused_supported(int M, int N, int K);
+int64_t linear_fused_workspace_bytes(int M);
+hipError_t launch_linear_fused(const uint16_t* X, const int32_t* perm, const uint8_t* Wq, const uint16_t* sw, int M,
+                               int N, int K, uint8_t* Xq, uint16_t* sx, uint16_t* Y, int* ws, hipStream_t stream);
 hipError_t launch_gemm_small_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K, int32_t* acc,
                                        hipStream_t stream);
 // W4A8 GEMM (gemm_w4a8.hip): Xq in kRowA8 rows, Wq in kRowW4A8 rows.  acc != nullptr: write

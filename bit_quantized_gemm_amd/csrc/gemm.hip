@@ -47,6 +47,7 @@
 #include <stdint.h>
 
 #include "atom_internal.h"
+#include "row_quant.h"
 
 namespace atom {
 namespace {
@@ -201,13 +202,15 @@ __device__ __forceinline__ uint16_t load_scale(const StageAddr<NDMA>& ad, int s,
 // last `rem` tiles are divided among `splits` pieces (the last piece also takes the INT8
 // group), each writing its fp32 tile sum, still carrying the factor 2 of the scale
 // products, tile-major to part[(piece split * rem + tile - full) * BM * BN].
-// NBUF stage buffers (3 .. 8) form the ring: NBUF - 1 stages of copies are in flight ahead of
-// the group being multiplied.
+// One output tile (or one split-K piece of it) of the tiled GEMM: tile `lin` in tile order, K piece
+// `split` of `nsplit`.  NBUF stage buffers (3 .. 8) form the ring: NBUF - 1 stages of copies are
+// in flight ahead of the group being multiplied.  The LDS is declared here, once per kernel that
+// calls this; a kernel that calls it for several tiles puts a workgroup barrier between them.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NBUF, bool kAcc>
-__global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(kAcc ? 1 : 2))) void gemm_w4a4_kernel(
-    const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx, const uint8_t* __restrict__ Wq,
-    const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out,
-    int full, int rem, int splits, float* __restrict__ part) {
+__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx,
+                                          const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ sw, int M, int N,
+                                          int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out, int lin,
+                                          int split, int nsplit, int full, int rem, float* __restrict__ part) {
   using T = Tile<BM, BN, WAVES_M, WAVES_N>;
   static_assert(NBUF >= 3 && NBUF <= 8, "ring of 3 to 8 stage buffers");
   // The stage buffers, each its own object: the compiler then knows that a copy into one does
@@ -244,28 +247,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   const int wave = tid >> 6;
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
-  // Work assignment.  Workgroups go to the 8 XCDs round-robin by id.  Each XCD gets an equal
-  // share of the split pieces followed by an equal share of the whole tiles, each share a
-  // contiguous run in tile order (so an XCD's L2 sees a compact block of X and W), and the
-  // pieces are dispatched first so that the whole tiles fill in behind them.
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int npieces = rem * splits;
-  const int nblocks = full + npieces;
-  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
-  const int qb = nblocks / kXcds, rb = nblocks % kXcds;   // workgroups on XCD x: qb + (x < rb)
-  const int qp = npieces / kXcds, rp = npieces % kXcds;   // pieces on XCD x: qp + (x < rp)
-  const int px = qp + (xcd < rp ? 1 : 0);
-  const int pbase = xcd * qp + min(xcd, rp);
-  int lin, split = 0, nsplit = 1;
-  if (local < px) {
-    const int piece = pbase + local;
-    lin = full + piece % rem;
-    split = piece / rem;
-    nsplit = splits;
-  } else {
-    lin = (xcd * qb + min(xcd, rb)) - pbase + (local - px);
-  }
   const bool is_piece = nsplit > 1;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int2 tc = tile_coords(lin, tiles_m, tiles_n);
   const int m0 = tc.x * BM, n0 = tc.y * BN;
   const int G = K / ATOM_GROUP;
@@ -544,6 +527,37 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   }
 }
 
+// The tiled GEMM: one workgroup per output tile or split-K piece.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NBUF, bool kAcc>
+__global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(kAcc ? 1 : 2))) void gemm_w4a4_kernel(
+    const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx, const uint8_t* __restrict__ Wq,
+    const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out,
+    int full, int rem, int splits, float* __restrict__ part) {
+  // Work assignment.  Workgroups go to the 8 XCDs round-robin by id.  Each XCD gets an equal
+  // share of the split pieces followed by an equal share of the whole tiles, each share a
+  // contiguous run in tile order (so an XCD's L2 sees a compact block of X and W), and the
+  // pieces are dispatched first so that the whole tiles fill in behind them.
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int npieces = rem * splits;
+  const int nblocks = full + npieces;
+  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int qb = nblocks / kXcds, rb = nblocks % kXcds;   // workgroups on XCD x: qb + (x < rb)
+  const int qp = npieces / kXcds, rp = npieces % kXcds;   // pieces on XCD x: qp + (x < rp)
+  const int px = qp + (xcd < rp ? 1 : 0);
+  const int pbase = xcd * qp + min(xcd, rp);
+  int lin, split = 0, nsplit = 1;
+  if (local < px) {
+    const int piece = pbase + local;
+    lin = full + piece % rem;
+    split = piece / rem;
+    nsplit = splits;
+  } else {
+    lin = (xcd * qb + min(xcd, rb)) - pbase + (local - px);
+  }
+  gemm_tile<BM, BN, WAVES_M, WAVES_N, NBUF, kAcc>(Xq, sx, Wq, sw, M, N, K, Y, acc_out, lin, split, nsplit, full, rem,
+                                                  part);
+}
+
 // 128 x 128 workgroup tile, 2 x 2 waves of 64 x 64 (2 x 2 MFMA tiles of 32 x 32 each).
 constexpr int kBM = 128, kBN = 128, kWavesM = 2, kWavesN = 2, kRing = 3;
 // Split-K.  Grids of fewer than kSplitMinTiles tiles split every tile, aiming at about one
@@ -599,6 +613,146 @@ __global__ __launch_bounds__(256) void gemm_splitk_finish_kernel(const float* __
   }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Activation quantize and GEMM in one persistent launch.
+//
+// One workgroup per resident slot.  Each first quantizes its own few token rows (exactly as
+// atom_quantize_act does, into Xq / sx), makes those stores visible at device scope and adds
+// their count to the ready count of their 64-row block (release).  Then it runs its share of
+// the 128 x 128 output tiles (the tiled GEMM's own XCD-aware order: each XCD takes a contiguous
+// run of tiles, its workgroups interleaved over the run), and before each tile waits until the
+// tile's row blocks are complete (acquire).  No workgroup waits before it has quantized its
+// rows, so with every workgroup resident (the grid is the resident count for an otherwise idle
+// GPU) every wait ends.  The wait is bounded all the same: one that gives up sets the
+// workspace's timeout flag and the workgroup goes on (the outputs are then not valid).  Leaving,
+// each workgroup counts itself on its XCD's exit counter; the last of an XCD counts the XCD on
+// the global one, and the last XCD resets every count, so the workspace is zero again for the
+// next call (and for a graph replay) without a memset.  Work items come from no shared queue:
+// device-scope atomics on one address serialize across the XCDs (a queue item per tile and row
+// group made the launch 2.5x slower than the two separate kernels).
+//
+// Workspace (int32 words, zero before the first call and after every call):
+//   [0] XCDs done, [1 .. 8] workgroups done per XCD, [9] timeout flag (sticky: set by a wait
+//   that gave up, never cleared by the kernel), [10] wait limit (0: default; > 0: that many
+//   polls; < 0: every wait gives up at once, a forced failure that exercises the flag),
+//   [16 + b] rows of 64-row block b quantized.
+constexpr int kLinXcdsDone = 0, kLinXcdDone = 1, kLinTimeout = 9, kLinWaitLimit = 10, kLinBlocks = 16;
+constexpr int kLinBlockRows = 64;
+constexpr int kLinDefaultPolls = 1 << 20;
+
+__device__ __forceinline__ int lin_load_acquire(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int CHUNKS, int PASSES>
+__global__ __launch_bounds__(kBM * 2) __attribute__((amdgpu_waves_per_eu(2))) void linear_fused_kernel(
+    const uint16_t* __restrict__ X, const int32_t* __restrict__ perm, const uint8_t* __restrict__ Wq,
+    const uint16_t* __restrict__ sw, int M, int N, int K, uint8_t* __restrict__ Xq, uint16_t* __restrict__ sx,
+    uint16_t* __restrict__ Y, int* __restrict__ ws, int rows_per_wg) {
+  static_assert(kBM + kBN == rowq::kThreads, "the GEMM tile's threads are the row quantizer's");
+  __shared__ __attribute__((aligned(16))) uint32_t qlds[rowq::staged_stride(CHUNKS * 8 * rowq::kThreads) * 8];
+  const int nwg = gridDim.x, b = blockIdx.x;
+
+  // ---- this workgroup's token rows [r0, r1) (rows_per_wg is a power of two: inside one 64-row
+  // block, or whole blocks)
+  const int r0 = (int)min((long long)b * rows_per_wg, (long long)M), r1 = min(r0 + rows_per_wg, M);
+  if (r0 < r1) {
+    rowq::RowQuant<CHUNKS, PASSES, kRowW4A4> rq(X, perm, M, K, Xq, sx, qlds);
+    rq.prefetch(r0);
+    for (int r = r0; r < r1; ++r) {
+      __syncthreads();                               // everyone finished reading the previous row
+      rq.stage();
+      __syncthreads();
+      if (r + 1 < r1) rq.prefetch(r + 1);
+      rq.quantize(r, 0, 1);
+    }
+    // every wave's code and scale stores complete and visible at device scope, then the rows
+    // are counted
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0)
+      for (int blk = r0 / kLinBlockRows; blk * kLinBlockRows < r1; ++blk)
+        __hip_atomic_fetch_add(ws + kLinBlocks + blk, min(r1, (blk + 1) * kLinBlockRows) - max(r0, blk * kLinBlockRows),
+                               __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- this workgroup's tiles: XCD x (workgroups b = x, x + 8, ...) takes a contiguous run of
+  // the tile order, its workgroups interleaved over it
+  const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN, tiles = tiles_m * tiles_n;
+  const int xcd = b % kXcds, local = b / kXcds;
+  const int nx = (nwg - xcd + kXcds - 1) / kXcds;                  // workgroups on this XCD
+  const int qt = tiles / kXcds, rt = tiles % kXcds;
+  const int t0 = xcd * qt + min(xcd, rt), t1 = t0 + qt + (xcd < rt ? 1 : 0);
+  const int limit_word = ws[kLinWaitLimit];
+  const int limit = limit_word > 0 ? limit_word : kLinDefaultPolls;
+  for (int lin = t0 + local; lin < t1; lin += nx) {
+    const int2 tc = tile_coords(lin, tiles_m, tiles_n);
+    if (threadIdx.x == 0) {
+      const int m0 = tc.x * kBM, m1 = min(m0 + kBM, M);
+      if (limit_word < 0) __hip_atomic_store(ws + kLinTimeout, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int blk = m0 / kLinBlockRows; limit_word >= 0 && blk * kLinBlockRows < m1; ++blk) {
+        const int want = min(kLinBlockRows, M - blk * kLinBlockRows);
+        int polls = 0;
+        while (lin_load_acquire(ws + kLinBlocks + blk) < want) {
+          if (++polls > limit) {
+            __hip_atomic_store(ws + kLinTimeout, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+    }
+    __syncthreads();                                 // the tile's rows are visible to every wave (and
+                                                     // the previous tile's LDS is free)
+    gemm_tile<kBM, kBN, kWavesM, kWavesN, kRing, false>(Xq, sx, Wq, sw, M, N, K, Y, nullptr, lin, 0, 1, tiles, 0,
+                                                        nullptr);
+  }
+
+  // ---- leave: the last workgroup of the last XCD resets every count for the next call
+  if (threadIdx.x == 0) {
+    const int xcds = min(nwg, kXcds);
+    const int done = __hip_atomic_fetch_add(ws + kLinXcdDone + xcd, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == nx - 1 &&
+        __hip_atomic_fetch_add(ws + kLinXcdsDone, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == xcds - 1) {
+      const int nblocks = (M + kLinBlockRows - 1) / kLinBlockRows;
+      for (int blk = 0; blk < nblocks; ++blk)
+        __hip_atomic_store(ws + kLinBlocks + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int x = 0; x < kXcds; ++x) __hip_atomic_store(ws + kLinXcdDone + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ws + kLinXcdsDone, 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+template <int CHUNKS, int PASSES>
+hipError_t launch_linear_fused_inst(const uint16_t* X, const int32_t* perm, const uint8_t* Wq, const uint16_t* sw,
+                                    int M, int N, int K, uint8_t* Xq, uint16_t* sx, uint16_t* Y, int* ws,
+                                    hipStream_t stream) {
+  // persistent: as many workgroups as are resident at once (queried once per process and
+  // instantiation on the device current at the first call)
+  static const int resident = [] {
+    int dev = 0, cus = 256, per_cu = 2;
+    if (hipGetDevice(&dev) == hipSuccess) {
+      int n = 0;
+      if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
+    }
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, linear_fused_kernel<CHUNKS, PASSES>, kBM * 2, 0) ==
+            hipSuccess && b > 0)
+      per_cu = b;
+    return cus * per_cu;
+  }();
+  // rows per workgroup: the least power of two that gives every row a workgroup; the grid is the
+  // resident count, fewer when there are fewer rows and tiles
+  const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  int rpw = 1;
+  while ((long long)rpw * resident < M) rpw *= 2;
+  const int grid = min(resident, max((M + rpw - 1) / rpw, tiles));
+  hipLaunchKernelGGL((linear_fused_kernel<CHUNKS, PASSES>), dim3(grid), dim3(kBM * 2), 0, stream, X, perm, Wq, sw, M,
+                     N, K, Xq, sx, Y, ws, rpw);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 GemmPlan gemm_plan(int M, int N, int K) {
@@ -652,6 +806,25 @@ hipError_t launch_splitk_finish(const float* part, const GemmPlan& plan, int M, 
   hipLaunchKernelGGL(kFinish[plan.splits], dim3(kBM * kBN / 4 / 256, plan.rem), dim3(256), 0, stream, part,
                      plan.full, plan.rem, M, N, Y);
   return hipGetLastError();
+}
+
+
+int64_t linear_fused_workspace_bytes(int M) {
+  const int64_t words = kLinBlocks + (M + kLinBlockRows - 1) / kLinBlockRows;
+  return (words * 4 + 255) / 256 * 256;
+}
+
+bool linear_fused_supported(int M, int N, int K) {
+  const GemmPlan plan = gemm_plan(M, N, K);
+  return !plan.small && !plan.tile64 && plan.rem == 0 && K <= 12288;
+}
+
+hipError_t launch_linear_fused(const uint16_t* X, const int32_t* perm, const uint8_t* Wq, const uint16_t* sw, int M,
+                               int N, int K, uint8_t* Xq, uint16_t* sx, uint16_t* Y, int* ws, hipStream_t stream) {
+  if (!linear_fused_supported(M, N, K)) return hipErrorInvalidValue;
+  if (K <= 4096) return launch_linear_fused_inst<2, 1>(X, perm, Wq, sw, M, N, K, Xq, sx, Y, ws, stream);
+  if (K <= 8192) return launch_linear_fused_inst<4, 2>(X, perm, Wq, sw, M, N, K, Xq, sx, Y, ws, stream);
+  return launch_linear_fused_inst<6, 3>(X, perm, Wq, sw, M, N, K, Xq, sx, Y, ws, stream);
 }
 
 hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K, int32_t* acc,

@@ -166,6 +166,34 @@ int atom_gemm_group_acc(const void *Xq, const void *Wq, int32_t M, int32_t N, in
                         int32_t *acc, void *stream);
 
 /*
+ * The layer's runtime forward in one call (a next step beside the path: the activation quantize
+ * fused with the GEMM, summary page, method paragraph: activations take their own quantize and
+ * outlier path on the way into the integer GEMM).  Computes exactly what atom_quantize_act
+ * (X, perm -> Xq, sx) followed by atom_gemm (-> Y) compute, with the same outputs.
+ *   X  : const fp16 [M, K]     perm : const int32 [K]
+ *   Wq : const uint8 [N, RB]   sw   : const fp16 [G, N]      (from atom_pack_weights)
+ *   Xq : uint8 [M, RB]         sx   : fp16 [G, M]            (outputs, as atom_quantize_act's)
+ *   Y  : fp16 [M, N]                                          (output)
+ *   workspace : atom_linear_workspace_bytes(M, N, K) bytes of device memory that must be zero
+ *               before its first use; every call leaves its control words zero again.
+ * When the GEMM runs whole 128 x 128 output tiles and K <= 12288, both steps run in ONE
+ * persistent launch: every workgroup first quantizes its share of the activation rows and
+ * counts them as ready, then runs its share of the output tiles, each after its rows are ready.
+ * No workgroup waits before its own rows are done, so the waits end when every workgroup is
+ * resident: the launch takes the resident count for an otherwise idle GPU.  The wait is bounded
+ * all the same: if one gives up (another kernel holding compute units meanwhile could cause
+ * that), int32 word 9 of the workspace becomes nonzero (read it after the stream completes; it
+ * stays set until the caller clears it) and the outputs of that call are not valid.  int32 word
+ * 10 sets the wait (0: default bound; > 0: that many polls; < 0: give up at once, which exercises
+ * the failure path).  Other shapes run the two kernels one after the other (the split-K scratch,
+ * if any, lies after the control words).  Calls sharing one workspace must not overlap (same
+ * stream, or synchronized).
+ */
+int64_t atom_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
+int atom_linear(const void *X, const int32_t *perm, const void *Wq, const void *sw, int32_t M, int32_t N, int32_t K,
+                void *Xq, void *sx, void *Y, void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * W4A8 variant (a next step beside the W4A4 path; the pages point to INT8 activations only as
  * the precision another method's kernels target).  Activations get INT8 codes in every group
  * (the rule of atom_quantize_act with qmax = 127 for every group); weights keep the W4 rule of

@@ -33,7 +33,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 19
     assert sorted(bq.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
