@@ -30,7 +30,7 @@ __all__ = [
     "atom_pack_weights", "atom_quantize_act", "atom_gemm", "atom_gemm_workspace_bytes", "atom_gemm_ws",
     "atom_gemm_group_acc", "linear", "atom_quantize_act_a8", "atom_pack_weights_w4a8", "atom_gemm_w4a8",
     "atom_gemm_w4a8_group_acc", "atom_gemm_w4a8_workspace_bytes", "atom_gemm_w4a8_ws",
-    "atom_linear_workspace_bytes", "atom_linear", "linear_timed_out",
+    "atom_linear_workspace_bytes", "atom_linear", "linear_timed_out", "atom_gemm_noalloc",
 ]
 
 GROUP = 128
@@ -43,7 +43,7 @@ EXPORTS = (
     "atom_pack_weights", "atom_quantize_act", "atom_gemm", "atom_gemm_workspace_bytes", "atom_gemm_ws",
     "atom_gemm_group_acc", "atom_quantize_act_a8", "atom_pack_weights_w4a8", "atom_gemm_w4a8",
     "atom_gemm_w4a8_group_acc", "atom_gemm_w4a8_workspace_bytes", "atom_gemm_w4a8_ws",
-    "atom_linear_workspace_bytes", "atom_linear",
+    "atom_linear_workspace_bytes", "atom_linear", "atom_gemm_noalloc",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +88,7 @@ def load_library():
         "atom_gemm_w4a8_ws": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp, i64, vp]),
         "atom_linear_workspace_bytes": (i64, [i32, i32, i32]),
         "atom_linear": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, i64, vp]),
+        "atom_gemm_noalloc": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -276,6 +277,16 @@ def atom_gemm_ws(Xq, sx, Wq, sw, K, workspace, Y=None, stream=None):
     (pX, pSx, pW, pSw, pY, pWs), M, N, Y, nws = _gemm_args(Xq, sx, Wq, sw, K, Y, "Y", torch.float16, workspace)
     _check(load_library().atom_gemm_ws(pX, pSx, pW, pSw, M, N, K, pY, pWs, nws, _stream(stream, Xq.device)),
            "atom_gemm_ws")
+    return Y
+
+
+def atom_gemm_noalloc(Xq, sx, Wq, sw, K, Y=None, stream=None):
+    """atom_gemm with the library's static split-K scratch: the C call allocates nothing (pass Y to
+    allocate nothing here either)."""
+    torch = _torch()
+    (pX, pSx, pW, pSw, pY, _), M, N, Y, _ = _gemm_args(Xq, sx, Wq, sw, K, Y, "Y", torch.float16)
+    _check(load_library().atom_gemm_noalloc(pX, pSx, pW, pSw, M, N, K, pY, _stream(stream, Xq.device)),
+           "atom_gemm_noalloc")
     return Y
 
 

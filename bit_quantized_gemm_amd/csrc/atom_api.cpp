@@ -79,6 +79,7 @@ const char* atom_strerror(int status) {
     case ATOM_E_ALIGN: return "a pointer is not 16-byte aligned";
     case ATOM_E_OVERLAP: return "an output buffer overlaps an input or another output";
     case ATOM_E_HIP: return "the HIP runtime reported an error when enqueuing a kernel";
+    case ATOM_E_SCRATCH: return "the shape needs more split-K scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -151,6 +152,28 @@ int atom_gemm_ws(const void* Xq, const void* sx, const void* Wq, const void* sw,
 int atom_gemm(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N, int32_t K, void* Y,
               void* stream) {
   return atom_gemm_ws(Xq, sx, Wq, sw, M, N, K, Y, nullptr, 0, stream);
+}
+
+int atom_gemm_noalloc(const void* Xq, const void* sx, const void* Wq, const void* sw, int32_t M, int32_t N, int32_t K,
+                      void* Y, void* stream) {
+  if (!Xq || !sx || !Wq || !sw || !Y) return ATOM_E_NULL;
+  if (!valid_gemm(M, N, K)) return ATOM_E_SHAPE;
+  if (!aligned16(Xq) || !aligned16(sx) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y)) return ATOM_E_ALIGN;
+  const atom::GemmPlan plan = atom::gemm_plan(M, N, K);
+  const int64_t need = atom::gemm_workspace_bytes(plan);
+  if (need > atom::static_scratch_bytes()) return ATOM_E_SCRATCH;
+  const uint64_t G = (uint64_t)K / ATOM_GROUP;
+  const uint64_t rb = (uint64_t)atom_row_bytes(K);
+  const Range in[4] = {range_of(Xq, (uint64_t)M * rb), range_of(sx, G * M * 2), range_of(Wq, (uint64_t)N * rb),
+                       range_of(sw, G * N * 2)};
+  const Range out[1] = {range_of(Y, (uint64_t)M * N * 2)};
+  if (int st = check_overlap(in, 4, out, 1)) return st;
+  void* part = nullptr;
+  if (need > 0 && atom::static_scratch_address(&part) != hipSuccess) return ATOM_E_HIP;
+  return hip_status(atom::launch_gemm(static_cast<const uint8_t*>(Xq), static_cast<const uint16_t*>(sx),
+                                      static_cast<const uint8_t*>(Wq), static_cast<const uint16_t*>(sw), M, N, K,
+                                      static_cast<uint16_t*>(Y), static_cast<float*>(part), plan,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int atom_gemm_group_acc(const void* Xq, const void* Wq, int32_t M, int32_t N, int32_t K, int32_t* acc,

@@ -65,6 +65,10 @@ int64_t gemm_workspace_bytes(const GemmPlan& plan);
 // `part` holds gemm_workspace_bytes(plan) bytes of scratch when that is > 0, else unused.
 hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
                        int K, uint16_t* Y, float* part, const GemmPlan& plan, hipStream_t stream);
+// The library's static split-K scratch (atom_gemm_noalloc): its size, and its device address on
+// the current device (looked up once per device; no allocation).
+int64_t static_scratch_bytes();
+hipError_t static_scratch_address(void** out);
 // Few-rows kernel (M <= kSmallMaxM), Y written directly.
 hipError_t launch_gemm_small(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M,
                              int N, int K, uint16_t* Y, hipStream_t stream);

@@ -46,6 +46,8 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "atom_internal.h"
 #include "row_quant.h"
 
@@ -753,6 +755,14 @@ hipError_t launch_linear_fused_inst(const uint16_t* X, const int32_t* perm, cons
   return hipGetLastError();
 }
 
+// Split-K scratch for callers that cannot allocate (atom_gemm_noalloc): the largest split plan
+// of any valid shape needs 340 partial tiles of 64 KiB (M = 17, N = 10753: 85 tiles in 4 pieces),
+// so 384 tiles cover every shape.  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code this name is not a device address: the address comes from
+// hipGetSymbolAddress, per device.
+constexpr size_t kStaticScratchBytes = (size_t)384 * kBM * kBN * sizeof(float);   // 24 MiB
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 }  // namespace
 
 GemmPlan gemm_plan(int M, int N, int K) {
@@ -825,6 +835,28 @@ hipError_t launch_linear_fused(const uint16_t* X, const int32_t* perm, const uin
   if (K <= 4096) return launch_linear_fused_inst<2, 1>(X, perm, Wq, sw, M, N, K, Xq, sx, Y, ws, stream);
   if (K <= 8192) return launch_linear_fused_inst<4, 2>(X, perm, Wq, sw, M, N, K, Xq, sx, Y, ws, stream);
   return launch_linear_fused_inst<6, 3>(X, perm, Wq, sw, M, N, K, Xq, sx, Y, ws, stream);
+}
+
+int64_t static_scratch_bytes() { return (int64_t)kStaticScratchBytes; }
+
+hipError_t static_scratch_address(void** out) {
+  // the device address of `scratch` on the current device, looked up once per device
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K, int32_t* acc,

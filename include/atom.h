@@ -58,7 +58,8 @@ enum {
                           GEMM with more than ATOM_MAX_TILES output tiles */
   ATOM_E_ALIGN = 3,    /* a pointer is not 16-byte aligned */
   ATOM_E_OVERLAP = 4,  /* an output range overlaps an input or another output range */
-  ATOM_E_HIP = 5       /* the HIP runtime reported an error when enqueuing */
+  ATOM_E_HIP = 5,      /* the HIP runtime reported an error when enqueuing */
+  ATOM_E_SCRATCH = 6   /* atom_gemm_noalloc: the shape needs more scratch than ATOM_STATIC_SCRATCH_BYTES */
 };
 
 /* Bytes of one packed row, (K-128)/2 + 128: the K-128 bulk channels at four bits each and
@@ -155,6 +156,21 @@ int64_t atom_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 int atom_gemm_ws(const void *Xq, const void *sx, const void *Wq, const void *sw,
                  int32_t M, int32_t N, int32_t K, void *Y, void *workspace,
                  int64_t workspace_bytes, void *stream);
+
+/*
+ * atom_gemm for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same kernels and the same result as
+ * atom_gemm_ws with enough workspace, bit for bit, but the split-K scratch is a static buffer
+ * inside the library, ATOM_STATIC_SCRATCH_BYTES per GPU, held from the first call on that GPU
+ * until the process ends.  No allocation of any kind happens in the call.  The buffer of the
+ * current device is used (the stream must belong to it).  Every call on one GPU shares that
+ * buffer, so calls that overlap on one GPU (different streams without synchronization) race and
+ * give wrong results.  ATOM_E_SCRATCH if the shape's split needs more than the buffer (no valid
+ * shape does: the largest needs 21.25 MiB); other errors as for atom_gemm.
+ */
+#define ATOM_STATIC_SCRATCH_BYTES (24 << 20)
+int atom_gemm_noalloc(const void *Xq, const void *sx, const void *Wq, const void *sw, int32_t M, int32_t N, int32_t K,
+                      void *Y, void *stream);
 
 /*
  * Per-group integer accumulators (verification aid): acc[g, m, n] = acc_g[m,n] as defined

@@ -15,7 +15,7 @@ import bit_quantized_gemm_amd as bq
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "atom.h")
 
-OK, E_NULL, E_SHAPE, E_ALIGN, E_OVERLAP, E_HIP = 0, 1, 2, 3, 4, 5
+OK, E_NULL, E_SHAPE, E_ALIGN, E_OVERLAP, E_HIP, E_SCRATCH = 0, 1, 2, 3, 4, 5, 6
 
 
 def _declared():
@@ -33,7 +33,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 20
     assert sorted(bq.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -60,7 +60,7 @@ def test_shape_helpers(lib):
 
 
 def test_strerror(lib):
-    for s in (OK, E_NULL, E_SHAPE, E_ALIGN, E_OVERLAP, E_HIP, 99):
+    for s in (OK, E_NULL, E_SHAPE, E_ALIGN, E_OVERLAP, E_HIP, E_SCRATCH, 99):
         msg = bq.atom_strerror(s)
         assert isinstance(msg, str) and msg
     assert bq.atom_strerror(OK) == "ok"
@@ -298,3 +298,31 @@ def test_binding_rejects_mis_sized_tensors(lib, monkeypatch):
         bq.atom_gemm(Xq, sx, Wq, sw, K)
     with pytest.raises(bq.AtomError, match="ROCm device"):
         bq.atom_gemm_w4a8_ws(z((M, K), dtype=u8), sx, Wq, sw, K, z((16,), dtype=u8))
+
+
+def test_gemm_noalloc_validation(lib):
+    """atom_gemm_noalloc rejects bad arguments on the host before any HIP call (the calls below
+    never reach the device: each fails validation)."""
+    g = lib.atom_gemm_noalloc
+    assert g(None, B, C, D, 4, 4, 256, E, S) == E_NULL
+    assert g(A, B, C, D, 4, 4, 256, None, S) == E_NULL
+    assert g(A, B, C, D, 4, 4, 300, E, S) == E_SHAPE
+    assert g(A, B, C, D, 0, 4, 256, E, S) == E_SHAPE
+    assert g(A, B, C, D + 2, 4, 4, 256, E, S) == E_ALIGN
+    assert g(A, B, C, D, 4, 4, 256, A + 16, S) == E_OVERLAP     # Y inside Xq
+    assert g(A, B, C, D, 33, 8448, 4096, C + 64, S) == E_OVERLAP   # a split shape: Y over Wq
+    assert "static buffer" in bq.atom_strerror(E_SCRATCH)
+
+
+def test_static_scratch_covers_every_split_plan(lib):
+    """The static split-K scratch (24 MiB) holds the workspace of the largest split plan any valid
+    shape asks for, so atom_gemm_noalloc never has to refuse a valid shape."""
+    text = open(HEADER).read()
+    cap = 24 << 20
+    assert re.search(r"#define ATOM_STATIC_SCRATCH_BYTES \(24 << 20\)", text)
+    worst = 0
+    for M in (17, 33, 64, 100, 128, 129, 191, 192, 255, 256, 320, 384, 640):
+        for N in range(64, 128 * 130, 64):
+            worst = max(worst, bq.atom_gemm_workspace_bytes(M, N, 32768))
+    assert 0 < worst <= cap
+    assert bq.atom_gemm_workspace_bytes(17, 10753, 32768) == 340 * 128 * 128 * 4 == worst
