@@ -92,6 +92,16 @@ __device__ __forceinline__ v16f mma_fp6(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 2, 2, 0, kScaleE8M0, 0, kScaleE8M0);
 }
 
+// One issue slot of the INT4 main loop: the scheduling region's MFMA first, then up to NV
+// vector ALU operations, then up to NDS LDS reads; the region ends here.
+#define ATOM_SLOT(NV, NDS)                                  \
+  do {                                                      \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      \
+    __builtin_amdgcn_sched_group_barrier(0x002, (NV), 0);   \
+    __builtin_amdgcn_sched_group_barrier(0x100, (NDS), 0);  \
+    __builtin_amdgcn_sched_barrier(0);                      \
+  } while (0)
+
 __device__ __forceinline__ v16i mma_i8(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c, 0, 0, 0);
 }
@@ -317,18 +327,18 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
     return kAcc ? v16f{} : __builtin_amdgcn_mfma_f32_32x32x8f16(sbj, sai, v16f{}, 0, 0, 0);
   };
   // Group sum of tile (i, j) -> Y accumulators (or, kAcc, to acc_out for group g).
-  auto apply = [&](int i, int j, const v16f& acc, const v16f& sp, int g) {
+  auto apply_element = [&](int i, int j, const v16f& acc, const v16f& sp, int g, int r) {
     if (kAcc) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * T::kWTM + i * 32 + acc_row(lane);
-        const int n = n0 + wn * T::kWTN + j * 32 + acc_col(lane, r >> 2) + (r & 3);
-        if (m < M && n < N) acc_out[((size_t)g * M + m) * N + n] = (int32_t)acc[r];   // exact integers
-      }
+      const int m = m0 + wm * T::kWTM + i * 32 + acc_row(lane);
+      const int n = n0 + wn * T::kWTN + j * 32 + acc_col(lane, r >> 2) + (r & 3);
+      if (m < M && n < N) acc_out[((size_t)g * M + m) * N + n] = (int32_t)acc[r];   // exact integers
     } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) yacc[i][j][r] = __builtin_fmaf(acc[r], sp[r], yacc[i][j][r]);
+      yacc[i][j][r] = __builtin_fmaf(acc[r], sp[r], yacc[i][j][r]);
     }
+  };
+  auto apply = [&](int i, int j, const v16f& acc, const v16f& sp, int g) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) apply_element(i, j, acc, sp, g, r);
   };
   auto finish_tile = [&](int i, int j, const v16f& acc, h4 sai, h4 sbj, int g) {
     apply(i, j, acc, scale_product(sai, sbj), g);
@@ -387,14 +397,24 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));             // buffer 0 read by this wave
   wg_barrier();                                                // ... and by all: it may be refilled
 
-  // INT4 group s in ring position P (stage s in buffer P).  A wave issues in order, so nothing
-  // may wait on the MFMA issued just before it.  Per tile row i: region a decodes A row i
-  // (and every B column at i = 0), reads the matching operands of stage s+1, issues the scale
-  // product and the two K=64 fp6 MFMAs of tile (i, 0), then applies tile (i-1, 1); region b
-  // issues the scale product and MFMAs of tile (i, 1), then applies tile (i, 0).  Each apply
-  // thus comes after three MFMAs that do not feed it, so a tile's sums (the exact group sum
-  // in fp32) and its scale product are complete when they are used, and no more than two
-  // tiles' sums and scale products are live at a time.  The scheduling fences keep this order.
+  // INT4 group s in ring position P (stage s in buffer P).  A wave issues in order and stalls
+  // on an instruction whose operand an MFMA still computes, so each group is laid out as six
+  // slots per tile row i, each one MFMA followed by vector work that does not depend on the
+  // MFMAs in flight:
+  //   1  scale product (i, 0)      decode A row i, first half (i = 0: and B column 0, first half)
+  //   2  tile (i, 0), K 0..63      decode A row i, second half (i = 0: B column 0, second half);
+  //                                read the next stage's B column 0 (i = 0)
+  //   3  tile (i, 0), K 64..127    apply tile (i-1, 1) (i > 0); read the next stage's A row i
+  //   4  scale product (i, 1)      decode B column 1 and read the next stage's (i = 0)
+  //   5  tile (i, 1), K 0..63      apply tile (i, 0), first half
+  //   6  tile (i, 1), K 64..127    apply tile (i, 0), second half; after the last row, read
+  //                                the next stage's scales
+  // An apply thus follows at least two MFMAs that do not feed it.  The group's last tile is
+  // applied after the barrier, by which time its MFMAs have finished.  Each slot is a
+  // scheduling region whose MFMA is pinned ahead of its vector work.  (Against the previous
+  // two-region layout, whose scheduler put each apply right behind the MFMA feeding it, this
+  // raises the cycles in which MFMA and vector work overlap by a third; the time of a whole
+  // Llama-7B layer changes by about 1%, since the chip runs these shapes at its power limit.)
   static_assert(T::kTN == 2, "tile rows are processed as pairs of 32x32 tiles");
   auto int4_group = [&](auto ring, int s) __attribute__((always_inline)) {
     constexpr int p = decltype(ring)::kCur, pn = decltype(ring)::kNext, p2 = decltype(ring)::kAfterNext;
@@ -405,36 +425,49 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
     __builtin_amdgcn_sched_barrier(0);
     dma_stage(ad, LA(p), LB(p), min(s + NBUF, G));            // past the row end: unused
     __builtin_amdgcn_sched_barrier(0);
-    v16f acc0, sp0, acc1, sp1;                                 // tiles (i, 0) and (i, 1)
-    v8i b0[2], b1[2];                                          // fp6 operands of the B columns
     h4 san[T::kTM], sbn[T::kTN];
+    v8i b0[2], b1[2];                                          // fp6 operands of the B columns
+    v16f acc1, sp1;
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i) {
-      const v8i a0 = fp6_operand(pa[i], 0), a1 = fp6_operand(pa[i], 1);
-      if (i == 0) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          b0[j] = fp6_operand(pb[j], 0);
-          b1[j] = fp6_operand(pb[j], 1);
-          pb[j] = read_b(LB(pn), j);
-        }
-        if (!kAcc) read_scales(LS(pn), san, sbn);
-      }
-      pa[i] = read_a(LA(pn), i);
+      v8i a0, a1;
+      v16f acc0, sp0;
       sp0 = scale_product(sa[i], sb[0]);
+      a0 = fp6_operand(pa[i], 0);
+      if (i == 0) b0[0] = fp6_operand(pb[0], 0);
+      ATOM_SLOT(16, 0);
       acc0 = mma_fp6(a0, b0[0], v16f{});
+      a1 = fp6_operand(pa[i], 1);
+      if (i == 0) {
+        b1[0] = fp6_operand(pb[0], 1);
+        pb[0] = read_b(LB(pn), 0);
+      }
+      ATOM_SLOT(16, 2);
       acc0 = mma_fp6(a1, b1[0], acc0);
       if (i > 0) apply(i - 1, 1, acc1, sp1, s);
-      __builtin_amdgcn_sched_barrier(0);
+      pa[i] = read_a(LA(pn), i);
+      ATOM_SLOT(16, 2);
       sp1 = scale_product(sa[i], sb[1]);
+      if (i == 0) {
+        b0[1] = fp6_operand(pb[1], 0);
+        b1[1] = fp6_operand(pb[1], 1);
+        pb[1] = read_b(LB(pn), 1);
+      }
+      ATOM_SLOT(16, 2);
       acc1 = mma_fp6(a0, b0[1], v16f{});
+#pragma unroll
+      for (int r = 0; r < 8; ++r) apply_element(i, 0, acc0, sp0, s, r);
+      ATOM_SLOT(8, 0);
       acc1 = mma_fp6(a1, b1[1], acc1);
-      apply(i, 0, acc0, sp0, s);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 8; r < 16; ++r) apply_element(i, 0, acc0, sp0, s, r);
+      if (i == T::kTM - 1 && !kAcc) read_scales(LS(pn), san, sbn);   // this group's are all used
+      ATOM_SLOT(8, 4);
     }
-    apply(T::kTM - 1, 1, acc1, sp1, s);
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kInFlight));   // own copy of stage s+2 landed, reads done
     wg_barrier();
+    apply(T::kTM - 1, 1, acc1, sp1, s);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i) sa[i] = san[i];
 #pragma unroll
