@@ -221,7 +221,8 @@ def hbm_copy_gbs(torch, dev, mib=1024, reps=10):
 
 
 class ClockSampler:
-    """Samples the GPU's current graphics clock (amdsmi) from a thread while work runs."""
+    """Samples the GPU's graphics clock, the mean clock of its XCDs and its socket power (amdsmi)
+    from a thread while work runs."""
 
     def __init__(self, index=0, period_s=0.002):
         self.samples, self.err, self.period = [], None, period_s
@@ -235,21 +236,33 @@ class ClockSampler:
         except Exception as e:                               # pragma: no cover
             self.err = f"amdsmi unavailable: {e}"
 
+    @staticmethod
+    def _num(v, hi):
+        return float(v) if isinstance(v, (int, float)) and 0 < v < hi else None
+
     def _read(self):
         smi = self._smi
+        clk = power = xcd = None
         try:
             m = smi.amdsmi_get_gpu_metrics_info(self._h)
             for k in ("current_gfxclk", "average_gfxclk_frequency"):
                 v = m.get(k)
                 if isinstance(v, (list, tuple)):
-                    v = [u for u in v if isinstance(u, (int, float)) and 0 < u < 10000]
+                    v = [u for u in v if self._num(u, 10000)]
                     v = float(np.mean(v)) if v else None
-                if isinstance(v, (int, float)) and 0 < v < 10000:
-                    return float(v)
+                clk = self._num(v, 10000)
+                if clk:
+                    break
+            power = self._num(m.get("current_socket_power"), 5000)
+            v = m.get("current_gfxclks")
+            if isinstance(v, (list, tuple)):
+                v = [u for u in v if self._num(u, 10000)]
+                xcd = float(np.mean(v)) if v else None
         except Exception:
             pass
-        c = smi.amdsmi_get_clock_info(self._h, smi.AmdSmiClkType.GFX)
-        return float(c["clk"])
+        if clk is None:
+            clk = float(smi.amdsmi_get_clock_info(self._h, smi.AmdSmiClkType.GFX)["clk"])
+        return clk, power, xcd
 
     def __enter__(self):
         import threading
@@ -259,7 +272,7 @@ class ClockSampler:
         def run():
             while not self._stop:
                 try:
-                    self.samples.append(self._read())
+                    self.samples.append(self._read() + (time.perf_counter(),))
                 except Exception as e:                       # pragma: no cover
                     self.err = str(e)
                     return
@@ -274,8 +287,23 @@ class ClockSampler:
             self._t.join()
         return False
 
+    def _median(self, j, skip_s=0.0):
+        t0 = self.samples[0][3] if self.samples else 0.0
+        v = [x[j] for x in self.samples if x[j] is not None and x[3] >= t0 + skip_s]
+        return float(np.median(v)) if v else None
+
+    def distinct(self, j, skip_s=0.0):
+        t0 = self.samples[0][3] if self.samples else 0.0
+        return len({x[j] for x in self.samples if x[j] is not None and x[3] >= t0 + skip_s})
+
     def median_mhz(self):
-        return float(np.median(self.samples)) if self.samples else None
+        return self._median(0)
+
+    def median_power_w(self, skip_s=0.0):
+        return self._median(1, skip_s)
+
+    def median_xcd_mhz(self, skip_s=0.0):
+        return self._median(2, skip_s)
 
 
 def quant_only(args, torch, bq, synth, dev, R):
@@ -475,6 +503,28 @@ def main():
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
     sclk = clk.median_mhz()
+    # each shape's GEMM alone, back to back for ~2.5 s: socket power and the mean XCD clock it
+    # runs at, from the readings after the first second (the firmware refreshes them a few times
+    # a second; the larger shapes run at the power limit, so the clock, not the nominal 2.4 GHz,
+    # sets the attainable peak)
+    under_load = {}
+    for s in sets:
+        c, w = s["copies"][0], s["w"]
+        with ClockSampler(period_s=0.005) as pc:
+            t_end_clk = time.perf_counter() + 2.5
+            i = 0
+            while time.perf_counter() < t_end_clk:
+                if w4a8:
+                    bq.atom_gemm_w4a8_ws(c["Xq"], c["sx"], c["Wq"], c["sw"], w.K, s["ws"], Y=c["Y"], stream=stream)
+                else:
+                    bq.atom_gemm_ws(c["Xq"], c["sx"], c["Wq"], c["sw"], w.K, s["ws"], Y=c["Y"], stream=stream)
+                i += 1
+                if i % 50 == 0:
+                    torch.cuda.synchronize()
+            torch.cuda.synchronize()
+        xclk = pc.median_xcd_mhz(1.0)
+        under_load[s["key"]] = {"socket_power_w": pc.median_power_w(1.0), "xcd_clk_mhz": xclk,
+                                "samples": len(pc.samples), "distinct_clk_readings": pc.distinct(2, 1.0)}
     copy_gbs = hbm_copy_gbs(torch, dev)
 
     ops_step = sum(s["w"].ops for s in sets)
@@ -502,6 +552,13 @@ def main():
             "eff_tops": round(w.ops / ((p["quant_us"] + p["gemm_us"]) * 1e-6) / 1e12, 1),
             "tokens_per_s": round(w.M / ((p["quant_us"] + p["gemm_us"]) * 1e-6), 0),
         }
+        ul = under_load.get(w.key, {})
+        if ul.get("xcd_clk_mhz"):
+            # the INT8 peak scaled to the clock this GEMM actually runs at (256 CUs x 8192 ops/clk)
+            peak_at_clk = 256 * ul["xcd_clk_mhz"] * 1e6 * 8192 / 1e12
+            ul = dict(ul, int8_peak_tops_at_clk=round(peak_at_clk, 1),
+                      gemm_frac_int8_peak_at_clk=round(w.ops / (p["gemm_us"] * 1e-6) / 1e12 / peak_at_clk, 4))
+        shapes[w.key]["gemm_alone_under_load"] = ul
 
     traffic = None
     tr = traffic_for_current_gemm()

@@ -34,10 +34,13 @@ hipError_t launch_row_quantize(const uint16_t* X, const int32_t* perm, int rows,
 // small != 0 instead selects the few-rows kernel (gemm_small.hip), which needs no scratch.
 // tile64 != 0 instead runs whole 64 x 64 output tiles (two waves of 32 x 64 each), for grids
 // that have too few 128 x 128 tiles to fill the GPU but enough 64 x 64 ones: no split, no scratch.
+// kpart != 0 instead runs whole 64 x 64 output tiles with four waves each, every wave a
+// quarter of the K range, added in LDS at the end: no scratch, no second kernel.
 struct GemmPlan {
   int full, rem, splits;
   int small;
   int tile64;
+  int kpart;
 };
 // Few-rows kernel: at most kSmallMaxM token rows.
 constexpr int kSmallMaxM = 16;

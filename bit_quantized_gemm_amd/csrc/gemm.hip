@@ -163,8 +163,9 @@ struct Tile {
   static constexpr int kTN = kWTN / 32;                // MFMA tiles per wave (columns)
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kDma = BM / kWaves / 16;        // LDS-DMA instructions per wave per stage and tile
+  static constexpr int kSPT = (BM + BN) / kThreads;    // scales per thread per stage
   static_assert(kWTM % 32 == 0 && kWTN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(BM + BN == kThreads, "one scale per thread per stage");
+  static_assert(kSPT * kThreads == BM + BN && kSPT >= 1 && kSPT <= 2, "one or two scales per thread per stage");
   static_assert(BM == BN && kDma * kWaves * 16 == BM, "each wave copies whole 16-row slabs of A and B");
 };
 
@@ -172,15 +173,15 @@ struct Tile {
 // rows [w * BM / W, (w + 1) * BM / W) of A and the same rows of B (W waves), 16 rows per
 // LDS-DMA instruction: lane i of instruction h lands at LDS row r = w * BM / W + 16h + i / 4,
 // position i % 4, so it loads chunk (i % 4) ^ chunk_swz(r) of that row.  Rows past M / N
-// repeat the last valid row.  Thread t < BM carries the activation scale of tile row t,
-// thread BM + u the weight scale of tile column u.
-template <int NDMA>
+// repeat the last valid row.  Scale slot t < BM carries the activation scale of tile row t,
+// slot BM + u the weight scale of tile column u; thread t holds slots t, t + threads, ...
+template <int NDMA, int NS>
 struct StageAddr {
   __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc;  // the workgroup's rows of Xq / Wq
   int a_voff[NDMA], b_voff[NDMA];          // byte offset of this lane's chunk in stage 0
   int lds_row0;                            // first LDS row of this wave's copy (wave-uniform)
-  const uint16_t* s_src;                   // this thread's scale in group 0
-  bool s_is_x;                             // activation (stride M) or weight (stride N) scale
+  const uint16_t* s_src[NS];               // this thread's scales in group 0
+  bool s_is_x[NS];                         // activation (stride M) or weight (stride N) scale
 };
 
 // One LDS-DMA instruction: lane i loads 16 bytes at voff + soff of the buffer and writes them
@@ -191,8 +192,8 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* 
 }
 
 // Copy stage s of this wave's rows into LDS (asynchronous; tracked by vmcnt).
-template <int NDMA>
-__device__ __forceinline__ void dma_stage(const StageAddr<NDMA>& ad, uint8_t* la, uint8_t* lb, int s) {
+template <int NDMA, int NS>
+__device__ __forceinline__ void dma_stage(const StageAddr<NDMA, NS>& ad, uint8_t* la, uint8_t* lb, int s) {
   const int soff = s * kStageBytes;
 #pragma unroll
   for (int h = 0; h < NDMA; ++h) {
@@ -201,12 +202,12 @@ __device__ __forceinline__ void dma_stage(const StageAddr<NDMA>& ad, uint8_t* la
   }
 }
 
-// This thread's scale of stage s (group min(s, G-1): the INT8 group fills two stages).
-template <int NDMA>
-__device__ __forceinline__ uint16_t load_scale(const StageAddr<NDMA>& ad, int s, int G, int M, int N) {
+// This thread's scale u of stage s (group min(s, G-1): the INT8 group fills two stages).
+template <int NDMA, int NS>
+__device__ __forceinline__ uint16_t load_scale(const StageAddr<NDMA, NS>& ad, int s, int G, int M, int N, int u) {
   const int g = min(s, G - 1);
   const size_t ox = (size_t)g * M, ow = (size_t)g * N;   // uniform
-  return ad.s_src[ad.s_is_x ? ox : ow];
+  return ad.s_src[u][ad.s_is_x[u] ? ox : ow];
 }
 
 // kAcc = false: Y output.  kAcc = true: write the per-group integer accumulators instead.
@@ -218,62 +219,85 @@ __device__ __forceinline__ uint16_t load_scale(const StageAddr<NDMA>& ad, int s,
 // `split` of `nsplit`.  NBUF stage buffers (3 .. 8) form the ring: NBUF - 1 stages of copies are
 // in flight ahead of the group being multiplied.  The LDS is declared here, once per kernel that
 // calls this; a kernel that calls it for several tiles puts a workgroup barrier between them.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NBUF, bool kAcc>
+// SUB > 1: the workgroup is SUB parts of WAVES_M x WAVES_N waves; part k takes the k-th 1/SUB
+// of the tile's INT4 groups (the last part also the INT8 group), each part with a ring of
+// stage buffers of its own.  Parts of one wave need no barrier in the loop; parts of several
+// share the workgroup barrier, and a part with one group fewer passes one extra barrier so
+// that every wave passes the same number.  The SUB partial tiles are then added through LDS
+// in part order: the wave of part t adds up and stores MFMA tile t of its wave tile (parts past
+// the wave tile's MFMA tile count only hand in partials).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NBUF, bool kAcc, int SUB = 1>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx,
                                           const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ sw, int M, int N,
                                           int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out, int lin,
                                           int split, int nsplit, int full, int rem, float* __restrict__ part) {
   using T = Tile<BM, BN, WAVES_M, WAVES_N>;
   static_assert(NBUF >= 3 && NBUF <= 8, "ring of 3 to 8 stage buffers");
+  static_assert(SUB == 1 || (!kAcc && T::kTM * T::kTN <= SUB && SUB * T::kWaves <= 2 * NBUF),
+                "K parts: at most one output MFMA tile per wave, partials fit the stage buffers");
   // The stage buffers, each its own object: the compiler then knows that a copy into one does
   // not write what is read from another, and waits only where a buffer is really shared.
   // Buffers past NBUF are never referenced and take no LDS.
-  __shared__ __attribute__((aligned(16))) uint8_t la0[BM * kLdsRow], la1[BM * kLdsRow], la2[BM * kLdsRow],
-      la3[BM * kLdsRow], la4[BM * kLdsRow], la5[BM * kLdsRow], la6[BM * kLdsRow], la7[BM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint8_t lb0[BN * kLdsRow], lb1[BN * kLdsRow], lb2[BN * kLdsRow],
-      lb3[BN * kLdsRow], lb4[BN * kLdsRow], lb5[BN * kLdsRow], lb6[BN * kLdsRow], lb7[BN * kLdsRow];
+  // (SUB parts side by side in each buffer)
+  __shared__ __attribute__((aligned(16))) uint8_t la0[SUB * BM * kLdsRow], la1[SUB * BM * kLdsRow],
+      la2[SUB * BM * kLdsRow], la3[SUB * BM * kLdsRow], la4[SUB * BM * kLdsRow], la5[SUB * BM * kLdsRow],
+      la6[SUB * BM * kLdsRow], la7[SUB * BM * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint8_t lb0[SUB * BN * kLdsRow], lb1[SUB * BN * kLdsRow],
+      lb2[SUB * BN * kLdsRow], lb3[SUB * BN * kLdsRow], lb4[SUB * BN * kLdsRow], lb5[SUB * BN * kLdsRow],
+      lb6[SUB * BN * kLdsRow], lb7[SUB * BN * kLdsRow];
   // sx rows, then sw columns, each as a ready scale operand
-  __shared__ __attribute__((aligned(16))) h4 ls0[BM + BN], ls1[BM + BN], ls2[BM + BN], ls3[BM + BN], ls4[BM + BN],
-      ls5[BM + BN], ls6[BM + BN], ls7[BM + BN];
-  auto LA = [&](int p) -> uint8_t* {
+  __shared__ __attribute__((aligned(16))) h4 ls0[SUB * (BM + BN)], ls1[SUB * (BM + BN)], ls2[SUB * (BM + BN)],
+      ls3[SUB * (BM + BN)], ls4[SUB * (BM + BN)], ls5[SUB * (BM + BN)], ls6[SUB * (BM + BN)], ls7[SUB * (BM + BN)];
+  const int tid = threadIdx.x;
+  const int sub = SUB > 1 ? __builtin_amdgcn_readfirstlane(tid / T::kThreads) : 0;   // this wave's K part
+  const int vtid = SUB > 1 ? tid % T::kThreads : tid;                                 // thread within the part
+  auto LA0 = [&](int p) -> uint8_t* {
     switch (p) {
       case 0: return la0; case 1: return la1; case 2: return la2; case 3: return la3;
       case 4: return la4; case 5: return la5; case 6: return la6; default: return la7;
     }
   };
-  auto LB = [&](int p) -> uint8_t* {
+  auto LB0 = [&](int p) -> uint8_t* {
     switch (p) {
       case 0: return lb0; case 1: return lb1; case 2: return lb2; case 3: return lb3;
       case 4: return lb4; case 5: return lb5; case 6: return lb6; default: return lb7;
     }
   };
-  auto LS = [&](int p) -> h4* {
+  auto LS0 = [&](int p) -> h4* {
     switch (p) {
       case 0: return ls0; case 1: return ls1; case 2: return ls2; case 3: return ls3;
       case 4: return ls4; case 5: return ls5; case 6: return ls6; default: return ls7;
     }
   };
+  auto LA = [&](int p) { return LA0(p) + sub * (BM * kLdsRow); };
+  auto LB = [&](int p) { return LB0(p) + sub * (BN * kLdsRow); };
+  auto LS = [&](int p) { return LS0(p) + sub * (BM + BN); };
+  // One barrier per group orders a stage's copies and reads among the waves sharing it; a
+  // one-wave K part has its stages to itself, and its own waits order them.
+  auto ring_barrier = [&]() {
+    if constexpr (SUB == 1 || T::kWaves > 1) wg_barrier();
+  };
 
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = vtid >> 6;
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
-  const bool is_piece = nsplit > 1;
+  const bool is_piece = SUB == 1 && nsplit > 1;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int2 tc = tile_coords(lin, tiles_m, tiles_n);
   const int m0 = tc.x * BM, n0 = tc.y * BN;
   const int G = K / ATOM_GROUP;
   // this workgroup's INT4 groups [ga, gb); the last piece also takes the INT8 group
-  const int ga = split * (G - 1) / nsplit, gb = (split + 1) * (G - 1) / nsplit;
-  const bool last_split = split == nsplit - 1;
+  const int kpart = SUB > 1 ? sub : split, nparts = SUB > 1 ? SUB : nsplit;
+  const int ga = kpart * (G - 1) / nparts, gb = (kpart + 1) * (G - 1) / nparts;
+  const bool last_split = kpart == nparts - 1;
   const int S = G + 1;                                  // stages per row
   const size_t rbytes = (size_t)S * kStageBytes;        // = (K-128)/2 + 128
   const int l32 = lane & 31;                            // row (A) / column (B) inside a 32x32 tile
   const int kh = lane >> 5;                             // which K half of an operand this lane supplies
 
   // ---- per-lane stage-copy addresses
-  StageAddr<T::kDma> ad;
+  StageAddr<T::kDma, T::kSPT> ad;
   {
     const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
     ad.a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(Xq + (size_t)m0 * rbytes), (short)0,
@@ -287,8 +311,12 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
       ad.a_voff[h] = min(r, rows_a - 1) * (int)rbytes + c;
       ad.b_voff[h] = min(r, rows_b - 1) * (int)rbytes + c;
     }
-    ad.s_is_x = tid < BM;
-    ad.s_src = kAcc ? nullptr : ad.s_is_x ? sx + min(m0 + tid, M - 1) : sw + min(n0 + tid - BM, N - 1);
+#pragma unroll
+    for (int u = 0; u < T::kSPT; ++u) {
+      const int t = vtid + u * T::kThreads;
+      ad.s_is_x[u] = t < BM;
+      ad.s_src[u] = kAcc ? nullptr : t < BM ? sx + min(m0 + t, M - 1) : sw + min(n0 + t - BM, N - 1);
+    }
   }
 
   v16f yacc[T::kTM][T::kTN];
@@ -373,29 +401,37 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
   // written to LDS at the start of group t-2 (its buffer's previous stage was read during group
   // t-NBUF-1; loads complete in order, so waiting for that scale waits only for the copies of
   // stages up to t-1, which the ring needs by then anyway).
-  constexpr int kPerStage = 2 * T::kDma + (kAcc ? 0 : 1);   // vector-memory operations per stage
+  constexpr int kPerStage = 2 * T::kDma + (kAcc ? 0 : T::kSPT);   // vector-memory operations per stage
   constexpr int kInFlight = (NBUF - 2) * kPerStage;         // at most this many once stage s+2 landed
   static_assert(kInFlight <= 63, "vmcnt range");
-  uint16_t sreg[NBUF];
+  uint16_t sreg[NBUF][T::kSPT];
+  auto scale_load = [&](int q, int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < T::kSPT; ++u) sreg[q][u] = load_scale(ad, stage, G, M, N, u);
+  };
+  auto scale_store = [&](int q) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < T::kSPT; ++u) LS(q)[vtid + u * T::kThreads] = scale_operand(sreg[q][u]);
+  };
 #pragma unroll
   for (int q = 0; q < NBUF; ++q) {
-    sreg[q] = kAcc ? (uint16_t)0 : load_scale(ad, ga + q, G, M, N);
+    if (!kAcc) scale_load(q, ga + q);
     __builtin_amdgcn_sched_barrier(0);
     dma_stage(ad, LA(q), LB(q), min(ga + q, G));
     __builtin_amdgcn_sched_barrier(0);
   }
   if (!kAcc) {
-    LS(0)[tid] = scale_operand(sreg[0]);
-    LS(1)[tid] = scale_operand(sreg[1]);
+    scale_store(0);
+    scale_store(1);
   }
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kInFlight));   // stages ga and ga+1 have landed
-  wg_barrier();
+  ring_barrier();
   v8i pa[T::kTM], pb[T::kTN];
   h4 sa[T::kTM], sb[T::kTN];
-  if (!kAcc) read_scales(ls0, sa, sb);
-  read_packed(la0, lb0, pa, pb);
+  if (!kAcc) read_scales(LS(0), sa, sb);
+  read_packed(LA(0), LB(0), pa, pb);
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));             // buffer 0 read by this wave
-  wg_barrier();                                                // ... and by all: it may be refilled
+  ring_barrier();                                              // ... and by all: it may be refilled
 
   // INT4 group s in ring position P (stage s in buffer P).  A wave issues in order and stalls
   // on an instruction whose operand an MFMA still computes, so each group is laid out as six
@@ -419,9 +455,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
   auto int4_group = [&](auto ring, int s) __attribute__((always_inline)) {
     constexpr int p = decltype(ring)::kCur, pn = decltype(ring)::kNext, p2 = decltype(ring)::kAfterNext;
     // scale of stage s+2 into its buffer (read during group s+1)
-    if (!kAcc) LS(p2)[tid] = scale_operand(sreg[p2]);
+    if (!kAcc) scale_store(p2);
     // refill buffer p (stage s was read during group s-1, before the last barrier)
-    if (!kAcc) sreg[p] = load_scale(ad, s + NBUF, G, M, N);
+    if (!kAcc) scale_load(p, s + NBUF);
     __builtin_amdgcn_sched_barrier(0);
     dma_stage(ad, LA(p), LB(p), min(s + NBUF, G));            // past the row end: unused
     __builtin_amdgcn_sched_barrier(0);
@@ -465,7 +501,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
       ATOM_SLOT(8, 4);
     }
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kInFlight));   // own copy of stage s+2 landed, reads done
-    wg_barrier();
+    ring_barrier();
     apply(T::kTM - 1, 1, acc1, sp1, s);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -477,6 +513,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
     int s = ga;
     for (; s + NBUF <= gb; s += NBUF) ring_turn<0, NBUF>(int4_group, s);
     ring_tail<0, NBUF>(int4_group, s, gb);
+    if constexpr (SUB > 1 && T::kWaves > 1)   // parts get floor or ceil of (G-1)/SUB groups
+      if (gb - ga < (G - 1 + SUB - 1) / SUB) wg_barrier();
   }
 
   // INT8 outlier group: stage G-1 (its packed operands are in pa / pb, the group's scales in
@@ -510,6 +548,61 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
   }
   __builtin_amdgcn_s_waitcnt(0);                    // no copy into LDS outlives the workgroup
 
+  // K parts: part v's partial of MFMA tile t goes to slot t of region v (stage buffer A v, or
+  // B v - NBUF), 16 floats per lane in the accumulator layout; the wave of part t then adds
+  // the SUB partials of tile t in part order, so the sum does not depend on timing.
+  if constexpr (SUB > 1) {
+    auto region = [&](int v) -> float* {   // v must fold to a constant: only buffers < NBUF exist
+      return reinterpret_cast<float*>(v < NBUF ? LA0(v) : LB0(v - NBUF));
+    };
+    constexpr int kRegions = SUB * T::kWaves;     // one per wave of the workgroup
+    const int me = sub * T::kWaves + wave;
+    float* mine = nullptr;
+#pragma unroll
+    for (int v = 0; v < kRegions; ++v)
+      if (v == me) mine = region(v);
+    __syncthreads();                                  // every part is done with the stage buffers
+#pragma unroll
+    for (int i = 0; i < T::kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::kTN; ++j) {
+        float* d = mine + ((i * T::kTN + j) * 64 + lane) * 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(d + 4 * q) =
+              float4{yacc[i][j][4 * q], yacc[i][j][4 * q + 1], yacc[i][j][4 * q + 2], yacc[i][j][4 * q + 3]};
+      }
+    __syncthreads();
+    v16f sum;
+    if (sub < T::kTM * T::kTN) {
+#pragma unroll
+    for (int v = 0; v < SUB; ++v) {
+      // the same wave position in part v (a compile-time region for each wave position)
+      const float* src = nullptr;
+#pragma unroll
+      for (int w = 0; w < T::kWaves; ++w)
+        if (w == wave) src = region(v * T::kWaves + w);
+      src += (sub * 64 + lane) * 16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 x = *reinterpret_cast<const float4*>(src + 4 * q);
+        if (v == 0) {
+          sum[4 * q] = x.x; sum[4 * q + 1] = x.y; sum[4 * q + 2] = x.z; sum[4 * q + 3] = x.w;
+        } else {
+          sum[4 * q] += x.x; sum[4 * q + 1] += x.y; sum[4 * q + 2] += x.z; sum[4 * q + 3] += x.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < T::kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::kTN; ++j)
+        if (i * T::kTN + j == sub) yacc[i][j] = sum;
+    }
+  }
+  // the MFMA tiles this wave stores (all of them, or with K parts the one it added up)
+  auto owns = [&](int i, int j) { return SUB == 1 || i * T::kTN + j == sub; };
+
   // Store.  Each lane writes four runs of four consecutive outputs per tile.  A split piece
   // writes its whole fp32 tile (16-byte stores; rows and columns past Y land in the piece's
   // own scratch tile and are never read).  A whole tile writes Y with 8-byte fp16 stores when
@@ -538,6 +631,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
         for (int j = 0; j < T::kTN; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
+            if (!owns(i, j)) continue;
             const int n = n0 + wn * T::kWTN + j * 32 + acc_col(lane, q);
             ushort4 o;
             o.x = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][4 * q]));
@@ -556,7 +650,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
           for (int r = 0; r < 16; ++r) {
             const int m = m0 + wm * T::kWTM + i * 32 + acc_row(lane);
             const int n = n0 + wn * T::kWTN + j * 32 + acc_col(lane, r >> 2) + (r & 3);
-            if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][r]));
+            if (owns(i, j) && m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(0.5f * yacc[i][j][r]));
           }
     }
   }
@@ -593,6 +687,19 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
                                                   part);
 }
 
+// One 64 x 64 output tile per workgroup of SUB K parts of WM x WN waves (see gemm_tile), for
+// grids that have too few tiles to give every SIMD a wave otherwise.
+template <int BM, int WM, int WN, int SUB, int NBUF>
+__global__ __launch_bounds__(SUB * WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a4_kpart_kernel(
+    const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx, const uint8_t* __restrict__ Wq,
+    const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int tiles) {
+  // whole tiles only: XCD x takes a contiguous run of the tile order (as gemm_w4a4_kernel does)
+  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int qb = tiles / kXcds, rb = tiles % kXcds;
+  const int lin = xcd * qb + min(xcd, rb) + local;
+  gemm_tile<BM, BM, WM, WN, NBUF, false, SUB>(Xq, sx, Wq, sw, M, N, K, Y, nullptr, lin, 0, 1, tiles, 0, nullptr);
+}
+
 // 128 x 128 workgroup tile, 2 x 2 waves of 64 x 64 (2 x 2 MFMA tiles of 32 x 32 each).
 constexpr int kBM = 128, kBN = 128, kWavesM = 2, kWavesN = 2, kRing = 3;
 // Split-K.  Grids of fewer than kSplitMinTiles tiles split every tile, aiming at about one
@@ -604,12 +711,23 @@ constexpr int kBM = 128, kBN = 128, kWavesM = 2, kWavesN = 2, kRing = 3;
 // 600 x 2048 x 15300 with 88 of 600 split three ways is slower).
 constexpr int kSplitMinTiles = 128, kSplitTargetBlocks = 256, kSplitMinGroups = 4, kSplitMax = 8;
 // 64 x 64 output tiles, two waves of 32 x 64 (one 32 x 32 MFMA tile row, two columns): for grids
-// with fewer than kSplitMinTiles tiles of 128 x 128 but at least k64MinTiles of 64 x 64, whole
-// small tiles replace split-K (no partial sums, no second kernel, no scratch).  Measured on
-// 256 x 4096 x 4096 (kernel trace): 16.0 us against 19.9 us for four split-K pieces of 128 x 128
-// plus 4.4 us for their finalize kernel.  A deeper ring does not help these tiles (event-timed:
-// 3 or 4 buffers 18.3 us, 6 buffers 21.5 us, 8 buffers 22.2 us), so they keep three.
+// with fewer than kSplitMinTiles tiles of 128 x 128 but at least k64MinTiles of 64 x 64 that
+// are too short for K parts (below), whole small tiles replace split-K (no partial sums, no
+// second kernel, no scratch).  Measured on 256 x 4096 x 4096 (kernel trace): 16.0 us against
+// 19.9 us for four split-K pieces of 128 x 128 plus 4.4 us for their finalize kernel.  A deeper
+// ring helps neither these tiles (event-timed: 3 or 4 buffers 18.3 us, 6 buffers 21.5 us, 8
+// buffers 22.2 us) nor the K parts (3 buffers 14.4 us, 4 buffers 14.6 us, four parts of four
+// buffers 14.7 us), so they keep three.  The group accumulators of both run on these tiles.
 constexpr int k64 = 64, k64WavesM = 2, k64WavesN = 1, k64Ring = 3, k64MinTiles = 192;
+// K parts: 64 x 64 tiles, two parts of two waves of 32 x 64 each taking half of the groups
+// (gemm_w4a4_kpart_kernel).  Grids of fewer than kSplitMinTiles tiles of 128 x 128 take them
+// when they have at least kPartTiles tiles of 64 x 64, or at least kPartMinTiles and no more
+// than kPartMaxGroups groups; otherwise split-K (more workgroups on a long K).  Measured
+// (kernel trace, split-K time including its finalize): 256x4096x4096 15.7 (whole 64 x 64
+// tiles) -> 12.7 us; 128x4096x4096 20.4 -> 12.0; 64x4096x4096 16.8 -> 11.6; 33x4096x8448
+// 21.6 -> 12.4; 64x4096x11008 21.9 -> 12.1; 17x32768x10753 64.4 -> 58.5; but 64x11008x4096
+// (64 tiles, 86 groups) 20.0 with split-K against 22.8.
+constexpr int kParts = 2, kPartMinGroups = 2 * kParts, kPartTiles = 128, kPartMinTiles = 64, kPartMaxGroups = 48;
 
 // Y of the split tiles = fp16(0.5 * sum over pieces of the partial tiles), pieces added in
 // order.  blockIdx.y = split tile (tile full + blockIdx.y in tile order); four consecutive
@@ -789,8 +907,9 @@ hipError_t launch_linear_fused_inst(const uint16_t* X, const int32_t* perm, cons
 }
 
 // Split-K scratch for callers that cannot allocate (atom_gemm_noalloc): the largest split plan
-// of any valid shape needs 340 partial tiles of 64 KiB (M = 17, N = 10753: 85 tiles in 4 pieces),
-// so 384 tiles cover every shape.  Each GPU the library runs on holds its own copy until the
+// of any valid shape needs 315 partial tiles of 64 KiB (63 tiles in 5 pieces, e.g. M = 17,
+// N = 8000, K = 32768; a split grid has at most 64 tiles when M <= 64 and 32 otherwise, since
+// grids of 128 tiles of 64 x 64 or more take K parts), so 384 tiles cover every shape.  Each GPU the library runs on holds its own copy until the
 // process ends.  In host code this name is not a device address: the address comes from
 // hipGetSymbolAddress, per device.
 constexpr size_t kStaticScratchBytes = (size_t)384 * kBM * kBN * sizeof(float);   // 24 MiB
@@ -802,6 +921,10 @@ GemmPlan gemm_plan(int M, int N, int K) {
   if (M <= kSmallMaxM) return GemmPlan{0, 0, 1, 1, 0};
   const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   const int tiles64 = ((M + k64 - 1) / k64) * ((N + k64 - 1) / k64);
+  const int G = K / ATOM_GROUP;
+  if (tiles < kSplitMinTiles && G - 1 >= kPartMinGroups &&
+      (tiles64 >= kPartTiles || (tiles64 >= kPartMinTiles && G <= kPartMaxGroups)))
+    return GemmPlan{tiles64, 0, 1, 0, 0, 1};
   if (tiles < kSplitMinTiles && tiles64 >= k64MinTiles) return GemmPlan{tiles64, 0, 1, 0, 1};
   return gemm_plan_tiled(M, N, K);
 }
@@ -815,13 +938,20 @@ GemmPlan gemm_plan_tiled(int M, int N, int K) {
 }
 
 int64_t gemm_workspace_bytes(const GemmPlan& plan) {
-  if (plan.small || plan.tile64) return 0;
+  if (plan.small || plan.tile64 || plan.kpart) return 0;
   return plan.rem > 0 ? (int64_t)plan.rem * plan.splits * kBM * kBN * (int64_t)sizeof(float) : 0;
 }
 
 hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
                        int K, uint16_t* Y, float* part, const GemmPlan& plan, hipStream_t stream) {
   if (plan.small) return launch_gemm_small(Xq, sx, Wq, sw, M, N, K, Y, stream);
+  if (plan.kpart) {
+    if (plan.rem != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_w4a4_kpart_kernel<k64, k64WavesM, k64WavesN, kParts, k64Ring>), dim3(plan.full),
+                       dim3(kParts * k64WavesM * k64WavesN * 64), 0, stream,
+                       Xq, sx, Wq, sw, M, N, K, Y, plan.full);
+    return hipGetLastError();
+  }
   if (plan.tile64) {
     if (plan.rem != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_w4a4_kernel<k64, k64, k64WavesM, k64WavesN, k64Ring, false>), dim3(plan.full),
@@ -859,7 +989,7 @@ int64_t linear_fused_workspace_bytes(int M) {
 
 bool linear_fused_supported(int M, int N, int K) {
   const GemmPlan plan = gemm_plan(M, N, K);
-  return !plan.small && !plan.tile64 && plan.rem == 0 && K <= 12288;
+  return !plan.small && !plan.tile64 && !plan.kpart && plan.rem == 0 && K <= 12288;
 }
 
 hipError_t launch_linear_fused(const uint16_t* X, const int32_t* perm, const uint8_t* Wq, const uint16_t* sw, int M,
@@ -896,7 +1026,7 @@ hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, in
                                  hipStream_t stream) {
   const GemmPlan plan = gemm_plan(M, N, K);
   if (plan.small) return launch_gemm_small_group_acc(Xq, Wq, M, N, K, acc, stream);
-  if (plan.tile64) {
+  if (plan.tile64 || plan.kpart) {   // the same 64 x 64 tiles, one workgroup of two waves each
     hipLaunchKernelGGL((gemm_w4a4_kernel<k64, k64, k64WavesM, k64WavesN, k64Ring, true>), dim3(plan.full),
                        dim3(k64WavesM * k64WavesN * 64), 0, stream, Xq, (const uint16_t*)nullptr, Wq,
                        (const uint16_t*)nullptr, M, N, K, (uint16_t*)nullptr, acc, plan.full, 0, 1, (float*)nullptr);

@@ -166,7 +166,7 @@ int atom_gemm_ws(const void *Xq, const void *sx, const void *Wq, const void *sw,
  * current device is used (the stream must belong to it).  Every call on one GPU shares that
  * buffer, so calls that overlap on one GPU (different streams without synchronization) race and
  * give wrong results.  ATOM_E_SCRATCH if the shape's split needs more than the buffer (no valid
- * shape does: the largest needs 21.25 MiB); other errors as for atom_gemm.
+ * shape does: the largest needs 19.7 MiB); other errors as for atom_gemm.
  */
 #define ATOM_STATIC_SCRATCH_BYTES (24 << 20)
 int atom_gemm_noalloc(const void *Xq, const void *sx, const void *Wq, const void *sw, int32_t M, int32_t N, int32_t K,

@@ -187,14 +187,18 @@ def test_gemm_workspace_query(lib):
     T = 128 * 128 * 4
     # 256 x 4096 output = 2 x 32 tiles of 128 x 128 but 4 x 64 of 64 x 64: whole small tiles, no scratch
     assert bq.atom_gemm_workspace_bytes(256, 4096, 4096) == 0
-    # 33 x 8448: 66 tiles of 128 x 128, 132 of 64 x 64 (too few): every 128 x 128 tile split four ways
-    assert bq.atom_gemm_workspace_bytes(33, 8448, 4096) == 66 * 4 * T
+    # 33 x 8448: 66 tiles of 128 x 128 but 132 of 64 x 64: K parts inside the workgroup, no scratch
+    assert bq.atom_gemm_workspace_bytes(33, 8448, 4096) == 0
+    # 64 x 4096, K = 11008: 64 tiles of 64 x 64 on a long K (86 groups): 32 tiles split eight ways
+    assert bq.atom_gemm_workspace_bytes(64, 4096, 11008) == 32 * 8 * T
+    assert bq.atom_gemm_workspace_bytes(64, 4096, 4096) == 0               # 64 small tiles, 32 groups: K parts
     assert bq.atom_gemm_workspace_bytes(64, 128, 4096) == 1 * 7 * T       # capped by 31 INT4 groups / 4
     # M <= 16: the few-rows kernel reduces its K ranges inside the workgroup: no scratch
     for M, N, K in [(1, 130, 1152), (1, 4096, 4096), (16, 4096, 11008), (3, 131, 2048), (16, 16, 32768)]:
         assert bq.atom_gemm_workspace_bytes(M, N, K) == 0
     assert bq.atom_gemm_workspace_bytes(17, 128, 4096) == 1 * 7 * T        # 17 rows: 128 x 128 tiles, split-K
-    assert bq.atom_gemm_workspace_bytes(90 * 128, 64, 4096) == 90 * 3 * T   # ceil(256 / 90) = 3; 180 small tiles
+    assert bq.atom_gemm_workspace_bytes(90 * 128, 64, 4096) == 0            # 180 small tiles: K parts
+    assert bq.atom_gemm_workspace_bytes(17, 8000, 32768) == 63 * 5 * T       # 126 small tiles, long K: ceil(256 / 63) = 5
     # 128 tiles or more, or too few groups to divide: no scratch
     assert bq.atom_gemm_workspace_bytes(128 * 128, 128, 4096) == 0
     assert bq.atom_gemm_workspace_bytes(2048, 4096, 11008) == 0
@@ -310,7 +314,7 @@ def test_gemm_noalloc_validation(lib):
     assert g(A, B, C, D, 0, 4, 256, E, S) == E_SHAPE
     assert g(A, B, C, D + 2, 4, 4, 256, E, S) == E_ALIGN
     assert g(A, B, C, D, 4, 4, 256, A + 16, S) == E_OVERLAP     # Y inside Xq
-    assert g(A, B, C, D, 33, 8448, 4096, C + 64, S) == E_OVERLAP   # a split shape: Y over Wq
+    assert g(A, B, C, D, 64, 4096, 11008, C + 64, S) == E_OVERLAP   # a split shape: Y over Wq
     assert "static buffer" in bq.atom_strerror(E_SCRATCH)
 
 
@@ -325,4 +329,4 @@ def test_static_scratch_covers_every_split_plan(lib):
         for N in range(64, 128 * 130, 64):
             worst = max(worst, bq.atom_gemm_workspace_bytes(M, N, 32768))
     assert 0 < worst <= cap
-    assert bq.atom_gemm_workspace_bytes(17, 10753, 32768) == 340 * 128 * 128 * 4 == worst
+    assert bq.atom_gemm_workspace_bytes(17, 8000, 32768) == 315 * 128 * 128 * 4 == worst

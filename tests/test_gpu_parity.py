@@ -320,7 +320,7 @@ def test_deterministic_and_side_stream():
 
 # --------------------------------------------------------------------------- split-K (atom_gemm_ws)
 # pieces per split tile: 7, 3, 2, 4, 5, 6, 8; every piece count has its own finalize instance
-SPLIT = [(64, 128, 4096), (200, 300, 2048), (17, 130, 1152), (33, 8448, 4096), (17, 64, 3072), (40, 200, 3456),
+SPLIT = [(64, 128, 4096), (200, 300, 2048), (17, 130, 1152), (64, 4096, 11008), (17, 64, 3072), (40, 200, 3456),
          (33, 250, 4352)]
 
 
@@ -344,15 +344,19 @@ def test_gemm_ws_split_matches_oracle(M, N, K):
     np.testing.assert_array_equal(Y.view(np.uint16), Y2.view(np.uint16))
 
 
-# Grids with few 128 x 128 tiles but at least 192 of 64 x 64 run whole 64 x 64 tiles (no split,
-# no scratch): the Llama-7B attention projection, ragged edges, and group counts that leave a
-# partial turn of the eight-stage ring (K = 640: 4 INT4 groups, 4096: 31, 1152: 8, 11008: 85).
-TILE64 = [(256, 4096, 4096), (200, 4000, 640), (130, 5000, 1152), (100, 6100, 11008), (255, 3100, 4096)]
+# Grids with few 128 x 128 tiles but enough of 64 x 64 run whole 64 x 64 tiles (no split, no
+# scratch).  With at least 4 INT4 groups each workgroup splits K between two parts (K parts): the
+# Llama-7B attention projection, ragged edges, odd and even INT4 group counts (the part with one
+# group fewer passes one extra barrier: K = 640: 4 INT4 groups, 4096: 31, 1152: 8, 11008: 85),
+# and shapes that split-K would otherwise take (128, 64 and 33 rows).  K = 256 and 512 leave
+# too few groups to divide and run whole tiles of two waves.
+TILE64 = [(256, 4096, 4096), (200, 4000, 640), (130, 5000, 1152), (100, 6100, 11008), (255, 3100, 4096),
+          (128, 4096, 4096), (64, 4096, 4096), (33, 8448, 4096), (100, 2048, 4096), (200, 4000, 512), (255, 3100, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", TILE64)
 def test_gemm_tile64_matches_oracle(M, N, K):
-    _say(f"[tile64] M={M} N={N} K={K}")
+    _say(f"[64 x 64 tiles] M={M} N={N} K={K}")
     assert bq.atom_gemm_workspace_bytes(M, N, K) == 0
     x, wt, _ = synth.make_linear(M, K, N, seed=5 * M + N + K)
     perm = np.random.default_rng(K + 7).permutation(K).astype(np.int32)

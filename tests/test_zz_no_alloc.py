@@ -34,8 +34,8 @@ def _operands(M, N, K, seed):
 
 
 def test_noalloc_matches_workspace_entry_point_twice():
-    # 33 x 8448: 66 tiles in 4 split pieces (17.3 MB of partials); then 64 x 2048: 16 tiles in 7
-    for M, N, K in [(33, 8448, 4096), (64, 2048, 4096)]:
+    # 64 x 4096 x 11008: 32 tiles in 8 split pieces (16.8 MB of partials); then 64 x 2048: 16 tiles in 7
+    for M, N, K in [(64, 4096, 11008), (64, 2048, 4096)]:
         print(f"[noalloc] M={M} N={N} K={K}", flush=True)
         need = bq.atom_gemm_workspace_bytes(M, N, K)
         assert need > 0, "the shape must use split-K scratch"
