@@ -359,6 +359,8 @@ def main():
     ap.add_argument("--workload", default="llama7b", choices=sorted(WORKLOAD_SETS))
     ap.add_argument("--rotate", type=int, default=4, help="resident input copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-power-sample", action="store_true",
+                    help="skip the per-shape power / clock sampling (for profiler runs)")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="rows per shape in the CPU oracle sample (2048: every row)")
     ap.add_argument("--path", default="separate", choices=["separate", "fused"],
                     help="separate: atom_quantize_act then atom_gemm_ws; fused: atom_linear (one persistent "
@@ -508,12 +510,13 @@ def main():
     # a second; the larger shapes run at the power limit, so the clock, not the nominal 2.4 GHz,
     # sets the attainable peak)
     under_load = {}
-    for s in sets:
-        c, w = s["copies"][0], s["w"]
+    for s in (sets if not args.no_power_sample else []):
+        w = s["w"]
         with ClockSampler(period_s=0.005) as pc:
             t_end_clk = time.perf_counter() + 2.5
             i = 0
             while time.perf_counter() < t_end_clk:
+                c = s["copies"][i % R]
                 if w4a8:
                     bq.atom_gemm_w4a8_ws(c["Xq"], c["sx"], c["Wq"], c["sw"], w.K, s["ws"], Y=c["Y"], stream=stream)
                 else:
