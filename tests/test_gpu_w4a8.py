@@ -91,7 +91,8 @@ def test_w4a8_pack_weights_bitexact(key):
     np.testing.assert_array_equal(host(sw4).view(np.uint16), host(sw).view(np.uint16))
 
 
-@pytest.mark.parametrize("M,N,K", [(16, 512, 1024), (37, 200, 384), (130, 129, 1152), (1, 3, 256)])
+# the last shape has 65 INT4 groups: the LDS-DMA ring kernel (pieces of at least 64 groups)
+@pytest.mark.parametrize("M,N,K", [(16, 512, 1024), (37, 200, 384), (130, 129, 1152), (1, 3, 256), (37, 200, 8448)])
 def test_w4a8_group_acc_bitexact(M, N, K):
     _say(f"[w4a8 acc] M={M} N={N} K={K}")
     x, wt, _ = synth.make_linear(M, K, N, seed=7 * M + N + K)
@@ -149,9 +150,10 @@ def test_w4a8_zero_rows():
     assert_y_close(Y, O.gemm_ref(qx, sxr, qw, swr), "W4A8 zero rows")
 
 
-# pieces per split tile 7, 3, 2, 4 (the attention projection), 5, 6, 8, and a 16-row batch
+# pieces per split tile 7, 3, 2, 4 (the attention projection), 5, 6, 8, and a 16-row batch; the
+# last shape splits 255 INT4 groups three ways, so its pieces (85 groups) take the ring kernel
 W8_SPLIT = [(64, 128, 4096), (200, 300, 2048), (17, 130, 1152), (256, 4096, 4096), (17, 64, 3072),
-            (40, 200, 3456), (33, 250, 4352), (16, 512, 4096)]
+            (40, 200, 3456), (33, 250, 4352), (16, 512, 4096), (129, 5504, 32768)]
 
 
 @pytest.mark.parametrize("M,N,K", W8_SPLIT)
