@@ -35,7 +35,8 @@ INT8_PEAK_TOPS = 256 * 2.4e9 * 8192 / 1e12      # 5033: 256 CUs x 2.4 GHz x 8192
 # slightly lower and the reported fraction slightly conservative).
 FP6_PEAK_TOPS = 256 * 2.4e9 * 16384 / 1e12      # 10066: dense fp6 / fp4 MFMA
 HBM_PEAK_GBS = 8000.0
-GEMM_SRC = os.path.join(ROOT, "bit_quantized_gemm_amd", "csrc", "gemm.hip")
+# the W4A4 GEMM kernels' sources: the kernel file and the LDS stage-ring helpers it includes
+GEMM_SRC = [os.path.join(ROOT, "bit_quantized_gemm_amd", "csrc", f) for f in ("gemm.hip", "lds_ring.h")]
 QUANT_SRC = os.path.join(ROOT, "bit_quantized_gemm_amd", "csrc", "quantize.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
 
@@ -54,8 +55,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def sha256(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+def sha256(paths):
+    """SHA-256 of one file, or of several files' bytes in the order given."""
+    h = hashlib.sha256()
+    for p in ([paths] if isinstance(paths, str) else paths):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
 
 
 def quant_bytes(M, K):
