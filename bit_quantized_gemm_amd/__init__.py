@@ -35,7 +35,7 @@ __all__ = [
 
 GROUP = 128
 OUTLIERS = 128
-MAX_K = 32768
+MAX_K = 65536
 
 # Every symbol declared in include/atom.h.
 EXPORTS = (

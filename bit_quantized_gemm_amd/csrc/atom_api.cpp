@@ -75,7 +75,7 @@ const char* atom_strerror(int status) {
   switch (status) {
     case ATOM_OK: return "ok";
     case ATOM_E_NULL: return "a required pointer is NULL";
-    case ATOM_E_SHAPE: return "invalid shape: K must be a multiple of 128 in [256, 32768] and rows in [1, 2^24]";
+    case ATOM_E_SHAPE: return "invalid shape: K must be a multiple of 128 in [256, 65536] and rows in [1, 2^24]";
     case ATOM_E_ALIGN: return "a pointer is not 16-byte aligned";
     case ATOM_E_OVERLAP: return "an output buffer overlaps an input or another output";
     case ATOM_E_HIP: return "the HIP runtime reported an error when enqueuing a kernel";

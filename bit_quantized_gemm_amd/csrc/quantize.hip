@@ -160,6 +160,8 @@ hipError_t launch_rq_fmt(const uint16_t* X, const int32_t* perm, int rows, int K
   if (K <= 8192) return launch_rq<4, 2, FMT>(X, perm, rows, K, Q, S, stream);
   if (K <= 12288) return launch_rq<6, 3, FMT>(X, perm, rows, K, Q, S, stream);
   if (K <= 16384) return launch_rq<8, 4, FMT>(X, perm, rows, K, Q, S, stream);
+  // longer rows read perm on every row; rows up to 32768 keep two workgroups per compute unit
+  if (K <= 32768) return launch_rq<16, 0, FMT>(X, perm, rows, K, Q, S, stream);
   return launch_rq<ATOM_MAX_K / 8 / kThreads, 0, FMT>(X, perm, rows, K, Q, S, stream);
 }
 

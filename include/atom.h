@@ -47,7 +47,7 @@ extern "C" {
 
 #define ATOM_GROUP 128        /* elements per quantization group (record, "Weight group size") */
 #define ATOM_OUTLIERS 128     /* high-precision outlier channels (record, "notes") */
-#define ATOM_MAX_K 32768      /* largest K the kernels stage in LDS */
+#define ATOM_MAX_K 65536      /* largest K: the row quantize stages a whole fp16 row (128 KiB) in LDS */
 #define ATOM_MAX_ROWS (1 << 24)
 #define ATOM_MAX_TILES (1 << 26) /* GEMM: ceil(M/128) * ceil(N/128) output tiles at most */
 

@@ -53,10 +53,11 @@ def test_shape_helpers(lib):
     assert bq.atom_row_bytes(256) == 192
     assert bq.atom_num_groups(4096) == 32
     assert bq.atom_num_groups(11008) == 86
-    for bad in (0, 128, 200, 4100, 32768 + 128, -256):
+    for bad in (0, 128, 200, 4100, bq.MAX_K + 128, -256):
         assert bq.atom_row_bytes(bad) == -E_SHAPE
         assert bq.atom_num_groups(bad) == -E_SHAPE
     assert bq.atom_row_bytes(32768) == (32768 - 128) // 2 + 128
+    assert bq.atom_row_bytes(bq.MAX_K) == (bq.MAX_K - 128) // 2 + 128
 
 
 def test_strerror(lib):
@@ -83,7 +84,7 @@ def test_quantize_validation(lib):
     assert _q(lib, A, None, 4, 256, C, D) == E_NULL
     assert _q(lib, A, B, 4, 256, None, D) == E_NULL
     assert _q(lib, A, B, 4, 256, C, None) == E_NULL
-    for K in (0, 128, 300, 32896):
+    for K in (0, 128, 300, bq.MAX_K + 128):
         assert _q(lib, A, B, 4, K, C, D) == E_SHAPE
     for M in (0, -1, (1 << 24) + 1):
         assert _q(lib, A, B, M, 256, C, D) == E_SHAPE
@@ -327,6 +328,6 @@ def test_static_scratch_covers_every_split_plan(lib):
     worst = 0
     for M in (17, 33, 64, 100, 128, 129, 191, 192, 255, 256, 320, 384, 640):
         for N in range(64, 128 * 130, 64):
-            worst = max(worst, bq.atom_gemm_workspace_bytes(M, N, 32768))
+            worst = max(worst, bq.atom_gemm_workspace_bytes(M, N, bq.MAX_K))
     assert 0 < worst <= cap
-    assert bq.atom_gemm_workspace_bytes(17, 8000, 32768) == 315 * 128 * 128 * 4 == worst
+    assert bq.atom_gemm_workspace_bytes(17, 8000, bq.MAX_K) == 315 * 128 * 128 * 4 == worst

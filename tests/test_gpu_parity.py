@@ -304,6 +304,35 @@ def test_max_k():
     assert_y_close(Y, O.gemm_ref(qx, sxr, qw, swr), "max K")
 
 
+def test_max_k_statistic_quantize_tiles_and_split():
+    """K = ATOM_MAX_K through what a long K takes beyond the few-rows kernel: the statistic and
+    the outlier selection (one flag byte per channel in LDS), the quantize's general
+    instantiation (a 128 KiB staged row, more rows than resident workgroups), the 128 x 128
+    kernel over 512 groups (accumulators bit-exact) and split-K."""
+    M, N, K = 300, 136, bq.MAX_K
+    x, wt, _ = synth.make_linear(M, K, N, seed=3)
+    _say(f"[max K] M={M} N={N} K={K}")
+    X = dev(x)
+    p = bq.atom_select_outliers(bq.atom_channel_stat(X))
+    perm = O.outlier_perm(x)
+    np.testing.assert_array_equal(host(p), perm)
+    Xq, sx = bq.atom_quantize_act(X, p)
+    Wq, sw = bq.atom_pack_weights(dev(wt), p)
+    qx, sxr = O.quantize_rows(x, perm)
+    qw, swr = O.quantize_rows(wt, perm)
+    np.testing.assert_array_equal(host(Xq), O.pack_rows(qx))
+    np.testing.assert_array_equal(host(sx).view(np.uint16), sxr.view(np.uint16))
+    np.testing.assert_array_equal(host(Wq), O.pack_rows(qw))
+    acc = host(bq.atom_gemm_group_acc(Xq[:130], Wq, K))
+    np.testing.assert_array_equal(acc, O.group_acc(qx[:130], qw))
+    y64 = O.gemm_ref(qx, sxr, qw, swr)
+    assert_y_close(host(bq.atom_gemm(Xq, sx, Wq, sw, K)), y64, "max K, whole tiles")
+    need = bq.atom_gemm_workspace_bytes(M, N, K)
+    assert need > 0, "this shape is expected to split"
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    assert_y_close(host(bq.atom_gemm_ws(Xq, sx, Wq, sw, K, ws)), y64, "max K, split-K")
+
+
 # --------------------------------------------------------------------------- determinism and streams
 def test_deterministic_and_side_stream():
     w, x, wt, perm = workload("A")

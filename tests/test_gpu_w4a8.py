@@ -115,7 +115,8 @@ def test_w4a8_gemm_full_output(key):
     assert_y_close(Y, O.gemm_ref(qx, sxr, qw, swr), f"W4A8 {key}")
 
 
-RAGGED = [(1, 1, 256), (3, 70, 256), (129, 255, 2048), (200, 300, 640), (33, 70, 12416), (9, 40, 32768)]
+RAGGED = [(1, 1, 256), (3, 70, 256), (129, 255, 2048), (200, 300, 640), (33, 70, 12416), (9, 40, 32768),
+          (33, 70, bq.MAX_K)]
 
 
 @pytest.mark.parametrize("M,N,K", RAGGED)
