@@ -10,8 +10,9 @@
 //
 // Work layout.  A workgroup owns 16 output columns.  K is cut into ranges of at most MAXG
 // INT4 groups (the last range also takes the INT8 outlier group): 4, or 6 when ranges of 4
-// would need more than 16 waves; the workgroup has one wave per range, at most 16, and a wave
-// takes every 16th range when there are more.  A wave issues every load of a range at once straight into registers (no LDS
+// would need more than 16 waves, or 8 (at most 4 waves) when there are more column blocks than
+// two workgroups of 8 waves per compute unit can hold at once; the workgroup has one wave per
+// range, at most 16, and a wave takes every 16th range when there are more.  A wave issues every load of a range at once straight into registers (no LDS
 // staging, no barrier), then runs one 16 x 16 x 128 fp6 MFMA per group.  At the end the waves'
 // fp32 sums meet in LDS and wave 0 adds them in wave order and writes Y: one kernel, no
 // scratch, deterministic.
@@ -66,6 +67,7 @@ __device__ __forceinline__ h4 scale_operand(uint16_t v) {
 }
 
 constexpr int kMaxWaves = 16;                // waves (K ranges in flight) per workgroup
+constexpr int kDeepMinBlocks = 512;          // column blocks beyond which ranges of 8 are taken
 
 // The kAcc stores sit under a per-lane branch (token rows past M store nothing).  Left alone,
 // the compiler sinks the operand decode and the MFMA that feed a store into that branch; the
@@ -78,7 +80,7 @@ __device__ __forceinline__ void keep_in_all_lanes(v4f& v) { asm volatile("" : "+
 // kAcc = true: write each group's exact integer sums to acc_out [G, M, N] instead of Y (the
 // same loads, decode and MFMAs; no scales are read).
 template <int MAXG, bool kAcc>
-__global__ __launch_bounds__(kMaxWaves * 64) void gemm_w4a4_small_kernel(const uint8_t* __restrict__ Xq,
+__global__ __launch_bounds__(MAXG == 8 ? 256 : kMaxWaves * 64) void gemm_w4a4_small_kernel(const uint8_t* __restrict__ Xq,
                                                                          const uint16_t* __restrict__ sx,
                                                                          const uint8_t* __restrict__ Wq,
                                                                          const uint16_t* __restrict__ sw, int M,
@@ -204,16 +206,24 @@ namespace {
 // (fewer waves that take a second range).  Measured on 16-token batches (event-timed): 16 x
 // 11008 x 4096 (85 INT4 groups) 11.3 -> 10.7 us with ranges of 6; with 31 INT4 groups ranges of
 // 6 are slower (16 x 4096 x 11008: 11.1 -> 11.4 us), and ranges of 2 are slower everywhere.
+// More than 512 column blocks with at most 32 INT4 groups: ranges of 8 in workgroups of at most
+// 4 waves (160 VGPRs, three workgroups per compute unit), so that every block is resident at
+// once instead of 1.34 rounds of 8-wave workgroups (kernel trace, 16 x 4096 x 11008: 8.96 ->
+// 8.17 us; its 688 blocks).
 template <bool kAcc>
 hipError_t launch_small(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
                         int K, uint16_t* Y, int32_t* acc, hipStream_t stream) {
   const int G = K / ATOM_GROUP;
   const bool wide = (G - 1 + 3) / 4 > kMaxWaves;
-  const int maxg = wide ? 6 : 4;
+  const bool deep = !wide && G - 1 <= 4 * 8 && (N + kCols - 1) / kCols > kDeepMinBlocks;
+  const int maxg = wide ? 6 : deep ? 8 : 4;
   const int ranges = (G - 1 + maxg - 1) / maxg;
   const int waves = ranges < kMaxWaves ? ranges : kMaxWaves;
   const dim3 grid((N + kCols - 1) / kCols), block(64 * waves);
-  if (wide)
+  if (deep)
+    hipLaunchKernelGGL((gemm_w4a4_small_kernel<8, kAcc>), grid, block, 0, stream, Xq, sx, Wq, sw, M, N, K, ranges, Y,
+                       acc);
+  else if (wide)
     hipLaunchKernelGGL((gemm_w4a4_small_kernel<6, kAcc>), grid, block, 0, stream, Xq, sx, Wq, sw, M, N, K, ranges, Y,
                        acc);
   else

@@ -205,6 +205,21 @@ def test_oracle_packed_units_every_code_in_every_field(M, N):
     assert_y_close(Y, O.gemm_ref(qx, sx, qw, sw), f"units {M}x{N}")
 
 
+@pytest.mark.parametrize("M,N,K", [(5, 8200, 1152), (16, 9000, 4224), (2, 11008, 4096)])
+def test_few_rows_wide_n_accumulators_bitexact(M, N, K):
+    """Few rows, many columns and at most 32 INT4 groups: the few-rows kernel's ranges of up to
+    8 groups (4 waves per workgroup).  Per-group accumulators bit-exact against the oracle."""
+    _say(f"[few rows acc] M={M} N={N} K={K}")
+    x, wt, _ = synth.make_linear(M, K, N, seed=M + N + 7 * K)
+    perm = np.random.default_rng(K + 1).permutation(K).astype(np.int32)
+    Xq, _ = bq.atom_quantize_act(dev(x), dev(perm))
+    Wq, _ = bq.atom_pack_weights(dev(wt), dev(perm))
+    acc = host(bq.atom_gemm_group_acc(Xq, Wq, K))
+    qx, _ = O.quantize_rows(x, perm)
+    qw, _ = O.quantize_rows(wt, perm)
+    np.testing.assert_array_equal(acc, O.group_acc(qx, qw))
+
+
 # --------------------------------------------------------------------------- a5: output
 @pytest.mark.parametrize("key", ["T", "A", "B", "C"])
 def test_gemm_full_output(key):
@@ -417,12 +432,12 @@ def test_gemm_ws_without_enough_scratch_is_atom_gemm():
 
 # --------------------------------------------------------------------------- few rows (M <= 16)
 SMALL = [(1, 4096, 4096), (16, 11008, 4096), (16, 4096, 11008), (3, 131, 2048), (7, 37, 256), (16, 16, 1152),
-         (5, 200, 32768), (12, 1000, 1408)]
+         (5, 200, 32768), (12, 1000, 1408), (3, 9000, 2048), (16, 8200, 4224)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL)
 def test_gemm_small_m_matches_oracle(M, N, K):
-    """M <= 16 runs the few-rows kernel (K ranges of at most 4 INT4 groups, one wave each, added
+    """M <= 16 runs the few-rows kernel (K ranges of 4, 6 or 8 INT4 groups, one wave each, added
     in LDS): Y against the oracle on up to 512 sampled columns (all of them for small N), and
     bit-identical on a second call and through atom_gemm_ws."""
     _say(f"[few rows] M={M} N={N} K={K}")
