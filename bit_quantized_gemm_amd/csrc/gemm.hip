@@ -65,6 +65,24 @@ constexpr int kStageBytes = 64;          // bytes of one stage of a packed row
 constexpr int kLdsRow = 64;              // bytes of one staged (packed) row in LDS
 constexpr int kXcds = 8;                 // accelerator complex dies (each with its own L2)
 constexpr int kScaleE8M0 = 127 + 3;      // 2^3: the e2m3 subnormal q / 8 counts as q
+constexpr int kFairBit = 8;              // real-time clock bit (100 MHz: 2.56 us period) of the turns
+
+// Issue priority 1 if bit 0 of b is set, else 0 (s_setprio takes only an immediate).  One asm
+// statement with its own skip, so the compiler's control flow and register allocation around
+// the main loop are untouched.
+__device__ __forceinline__ void set_priority_from_bit0(uint32_t b) {
+  asm volatile(
+      "s_bitcmp1_b32 %0, 0\n\t"
+      "s_cbranch_scc0 1f\n\t"
+      "s_setprio 1\n\t"
+      "s_branch 2f\n"
+      "1:\n\t"
+      "s_setprio 0\n"
+      "2:"
+      :
+      : "s"(b)
+      : "scc");
+}
 
 // fp6 operand (32 codes, six words) of the two packed units in words 4h .. 4h+3 of w: unit
 // words (w0, w1) -> fields T0 = w0 & ~kFp6Exp0, T1 = w1 & ~kFp6Exp1,
@@ -183,11 +201,12 @@ __device__ __forceinline__ uint16_t load_scale(const StageAddr<NDMA, NS>& ad, in
 // that every wave passes the same number.  The SUB partial tiles are then added through LDS
 // in part order: the wave of part t adds up and stores MFMA tile t of its wave tile (parts past
 // the wave tile's MFMA tile count only hand in partials).
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NBUF, bool kAcc, int SUB = 1>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NBUF, bool kAcc, int SUB = 1, bool kFair = false>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx,
                                           const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ sw, int M, int N,
                                           int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out, int lin,
-                                          int split, int nsplit, int full, int rem, float* __restrict__ part) {
+                                          int split, int nsplit, int full, int rem, float* __restrict__ part,
+                                          int fair_cus = 0) {
   using T = Tile<BM, BN, WAVES_M, WAVES_N>;
   static_assert(NBUF >= 3 && NBUF <= 8, "ring of 3 to 8 stage buffers");
   static_assert(SUB == 1 || (!kAcc && T::kTM * T::kTN <= SUB && SUB * T::kWaves <= 2 * NBUF),
@@ -409,8 +428,15 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
   // raises the cycles in which MFMA and vector work overlap by a third; the time of a whole
   // Llama-7B layer changes by about 1%, since the chip runs these shapes at its power limit.)
   static_assert(T::kTN == 2, "tile rows are processed as pairs of 32x32 tiles");
+  // Fair turns (kFair: a grid of one round with two workgroups on some compute units).  A SIMD
+  // issues the older of two ready waves first, so of two workgroups sharing a compute unit the
+  // one dispatched first runs ahead and the other finishes alone.  Workgroups b and
+  // b + fair_cus (the first and second on a compute unit) instead take priority 1 in turns, by a
+  // bit of the real-time clock read at the start of each group and applied after its barrier.
+  const uint32_t fair_parity = kFair ? (blockIdx.x / (unsigned)fair_cus) & 1u : 0u;
   auto int4_group = [&](auto ring, int s) __attribute__((always_inline)) {
     constexpr int p = decltype(ring)::kCur, pn = decltype(ring)::kNext, p2 = decltype(ring)::kAfterNext;
+    const uint32_t tnow = kFair ? (uint32_t)__builtin_amdgcn_s_memrealtime() : 0u;
     // scale of stage s+2 into its buffer (read during group s+1)
     if (!kAcc) scale_store(p2);
     // refill buffer p (stage s was read during group s-1, before the last barrier)
@@ -459,6 +485,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
     }
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kInFlight));   // own copy of stage s+2 landed, reads done
     ring_barrier();
+    if constexpr (kFair) set_priority_from_bit0((tnow >> kFairBit) ^ fair_parity);
     apply(T::kTM - 1, 1, acc1, sp1, s);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -614,11 +641,11 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
 }
 
 // The tiled GEMM: one workgroup per output tile or split-K piece.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NBUF, bool kAcc>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NBUF, bool kAcc, bool kFair = false>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(kAcc ? 1 : 2))) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx, const uint8_t* __restrict__ Wq,
     const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out,
-    int full, int rem, int splits, float* __restrict__ part) {
+    int full, int rem, int splits, float* __restrict__ part, int fair_cus) {
   // Work assignment.  Workgroups go to the 8 XCDs round-robin by id.  Each XCD gets an equal
   // share of the split pieces followed by an equal share of the whole tiles, each share a
   // contiguous run in tile order (so an XCD's L2 sees a compact block of X and W), and the
@@ -640,8 +667,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_
   } else {
     lin = (xcd * qb + min(xcd, rb)) - pbase + (local - px);
   }
-  gemm_tile<BM, BN, WAVES_M, WAVES_N, NBUF, kAcc>(Xq, sx, Wq, sw, M, N, K, Y, acc_out, lin, split, nsplit, full, rem,
-                                                  part);
+  gemm_tile<BM, BN, WAVES_M, WAVES_N, NBUF, kAcc, 1, kFair>(Xq, sx, Wq, sw, M, N, K, Y, acc_out, lin, split, nsplit,
+                                                            full, rem, part, fair_cus);
 }
 
 // One 64 x 64 output tile per workgroup of SUB K parts of WM x WN waves (see gemm_tile), for
@@ -899,6 +926,21 @@ int64_t gemm_workspace_bytes(const GemmPlan& plan) {
   return plan.rem > 0 ? (int64_t)plan.rem * plan.splits * kBM * kBN * (int64_t)sizeof(float) : 0;
 }
 
+namespace {
+// Compute units of the device current at the first call (queried once per process; the
+// initialisation of a function-local static is thread-safe).  256 if the query fails.
+int compute_units() {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        n > 0)
+      return n;
+    return 256;
+  }();
+  return cus;
+}
+}  // namespace
+
 hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
                        int K, uint16_t* Y, float* part, const GemmPlan& plan, hipStream_t stream) {
   if (plan.small) return launch_gemm_small(Xq, sx, Wq, sw, M, N, K, Y, stream);
@@ -913,14 +955,24 @@ hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq,
     if (plan.rem != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_w4a4_kernel<k64, k64, k64WavesM, k64WavesN, k64Ring, false>), dim3(plan.full),
                        dim3(k64WavesM * k64WavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr,
-                       plan.full, 0, 1, (float*)nullptr);
+                       plan.full, 0, 1, (float*)nullptr, 0);
     return hipGetLastError();
   }
   if (plan.rem > 0 && (plan.splits < 2 || plan.splits > kSplitMax)) return hipErrorInvalidValue;
   const int blocks = plan.full + plan.rem * plan.splits;
-  hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, kRing, false>), dim3(blocks),
-                     dim3(kWavesM * kWavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr,
-                     plan.full, plan.rem, plan.splits, part);
+  // Fair turns (a kernel of their own) for a grid of one round: at most two workgroups on every
+  // compute unit, some with two.  With more rounds an early finish lets a later tile start
+  // sooner, which is worth more.  Event-timed, 2048 x 11008 x 4096 (512 tiles on 256 compute
+  // units): 87.1 -> 85.2 us; 1024 x 4096 x 11008 (688 tiles) ran 60.3 -> 61.7 us with them.
+  const int cus = compute_units();
+  if (blocks > cus && blocks <= 2 * cus)
+    hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, kRing, false, true>), dim3(blocks),
+                       dim3(kWavesM * kWavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr,
+                       plan.full, plan.rem, plan.splits, part, cus);
+  else
+    hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, kRing, false>), dim3(blocks),
+                       dim3(kWavesM * kWavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr,
+                       plan.full, plan.rem, plan.splits, part, 0);
   if (plan.rem > 0) return launch_splitk_finish(part, plan, M, N, Y, stream);
   return hipGetLastError();
 }
@@ -986,13 +1038,14 @@ hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, in
   if (plan.tile64 || plan.kpart) {   // the same 64 x 64 tiles, one workgroup of two waves each
     hipLaunchKernelGGL((gemm_w4a4_kernel<k64, k64, k64WavesM, k64WavesN, k64Ring, true>), dim3(plan.full),
                        dim3(k64WavesM * k64WavesN * 64), 0, stream, Xq, (const uint16_t*)nullptr, Wq,
-                       (const uint16_t*)nullptr, M, N, K, (uint16_t*)nullptr, acc, plan.full, 0, 1, (float*)nullptr);
+                       (const uint16_t*)nullptr, M, N, K, (uint16_t*)nullptr, acc, plan.full, 0, 1, (float*)nullptr,
+                       0);
     return hipGetLastError();
   }
   const dim3 grid(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM));
   hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, kRing, true>), grid, dim3(kWavesM * kWavesN * 64), 0,
                      stream, Xq, (const uint16_t*)nullptr, Wq, (const uint16_t*)nullptr, M, N, K,
-                     (uint16_t*)nullptr, acc, (int)grid.x, 0, 1, (float*)nullptr);
+                     (uint16_t*)nullptr, acc, (int)grid.x, 0, 1, (float*)nullptr, 0);
   return hipGetLastError();
 }
 
