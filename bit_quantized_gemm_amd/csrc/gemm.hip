@@ -645,7 +645,12 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int NBUF, bool kAcc, bool kF
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(kAcc ? 1 : 2))) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ Xq, const uint16_t* __restrict__ sx, const uint8_t* __restrict__ Wq,
     const uint16_t* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ Y, int32_t* __restrict__ acc_out,
-    int full, int rem, int splits, float* __restrict__ part, int fair_cus) {
+    int full, int rem, int splits, float* __restrict__ part, int fair_cus, int late_from) {
+  // Workgroups of later rounds (id >= late_from) issue at priority 1: a late tile shares its
+  // compute unit with a partner already part way through, and should not wait behind it (the
+  // older wave wins otherwise), so the two finish closer together.  1024 x 4096 x 11008 (688
+  // tiles for 512 slots, event-timed): 60.6-61.3 -> 59.7-60.0 us.
+  if (!kFair) set_priority_from_bit0((uint32_t)__builtin_amdgcn_readfirstlane((int)blockIdx.x >= late_from ? 1 : 0));
   // Work assignment.  Workgroups go to the 8 XCDs round-robin by id.  Each XCD gets an equal
   // share of the split pieces followed by an equal share of the whole tiles, each share a
   // contiguous run in tile order (so an XCD's L2 sees a compact block of X and W), and the
@@ -955,7 +960,7 @@ hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq,
     if (plan.rem != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_w4a4_kernel<k64, k64, k64WavesM, k64WavesN, k64Ring, false>), dim3(plan.full),
                        dim3(k64WavesM * k64WavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr,
-                       plan.full, 0, 1, (float*)nullptr, 0);
+                       plan.full, 0, 1, (float*)nullptr, 0, plan.full);
     return hipGetLastError();
   }
   if (plan.rem > 0 && (plan.splits < 2 || plan.splits > kSplitMax)) return hipErrorInvalidValue;
@@ -968,11 +973,11 @@ hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq,
   if (blocks > cus && blocks <= 2 * cus)
     hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, kRing, false, true>), dim3(blocks),
                        dim3(kWavesM * kWavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr,
-                       plan.full, plan.rem, plan.splits, part, cus);
+                       plan.full, plan.rem, plan.splits, part, cus, blocks);
   else
     hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, kRing, false>), dim3(blocks),
                        dim3(kWavesM * kWavesN * 64), 0, stream, Xq, sx, Wq, sw, M, N, K, Y, (int32_t*)nullptr,
-                       plan.full, plan.rem, plan.splits, part, 0);
+                       plan.full, plan.rem, plan.splits, part, 0, blocks > 2 * cus ? 2 * cus : blocks);
   if (plan.rem > 0) return launch_splitk_finish(part, plan, M, N, Y, stream);
   return hipGetLastError();
 }
@@ -1039,13 +1044,13 @@ hipError_t launch_gemm_group_acc(const uint8_t* Xq, const uint8_t* Wq, int M, in
     hipLaunchKernelGGL((gemm_w4a4_kernel<k64, k64, k64WavesM, k64WavesN, k64Ring, true>), dim3(plan.full),
                        dim3(k64WavesM * k64WavesN * 64), 0, stream, Xq, (const uint16_t*)nullptr, Wq,
                        (const uint16_t*)nullptr, M, N, K, (uint16_t*)nullptr, acc, plan.full, 0, 1, (float*)nullptr,
-                       0);
+                       0, plan.full);
     return hipGetLastError();
   }
   const dim3 grid(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM));
   hipLaunchKernelGGL((gemm_w4a4_kernel<kBM, kBN, kWavesM, kWavesN, kRing, true>), grid, dim3(kWavesM * kWavesN * 64), 0,
                      stream, Xq, (const uint16_t*)nullptr, Wq, (const uint16_t*)nullptr, M, N, K,
-                     (uint16_t*)nullptr, acc, (int)grid.x, 0, 1, (float*)nullptr, 0);
+                     (uint16_t*)nullptr, acc, (int)grid.x, 0, 1, (float*)nullptr, 0, (int)grid.x);
   return hipGetLastError();
 }
 
