@@ -65,7 +65,7 @@ constexpr int kStageBytes = 64;          // bytes of one stage of a packed row
 constexpr int kLdsRow = 64;              // bytes of one staged (packed) row in LDS
 constexpr int kXcds = 8;                 // accelerator complex dies (each with its own L2)
 constexpr int kScaleE8M0 = 127 + 3;      // 2^3: the e2m3 subnormal q / 8 counts as q
-constexpr int kFairBit = 8;              // real-time clock bit (100 MHz: 2.56 us period) of the turns
+constexpr int kFairBit = 9;              // real-time clock bit (100 MHz: 5.12 us period) of the turns
 
 // Issue priority 1 if bit 0 of b is set, else 0 (s_setprio takes only an immediate).  One asm
 // statement with its own skip, so the compiler's control flow and register allocation around
