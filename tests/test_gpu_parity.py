@@ -265,7 +265,9 @@ def test_gemm_llama70b_sampled():
 
 # --------------------------------------------------------------------------- ragged / edge shapes
 RAGGED = [(1, 1, 256), (2, 3, 256), (37, 200, 384), (130, 129, 1152), (257, 513, 640), (16, 512, 1024),
-          (128, 128, 256), (129, 255, 2048), (33, 70, 12416), (20, 48, 16384), (9, 40, 20480)]
+          (128, 128, 256), (129, 255, 2048), (33, 70, 12416), (20, 48, 16384), (9, 40, 20480),
+          # 288 tiles: one round, the fair-turns kernel; 860 tiles: several rounds, later ones at priority 1
+          (1100, 4000, 640), (1200, 11000, 384)]
 
 
 @pytest.mark.parametrize("M,N,K", RAGGED)
