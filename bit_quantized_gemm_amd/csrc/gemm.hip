@@ -84,6 +84,26 @@ __device__ __forceinline__ void set_priority_from_bit0(uint32_t b) {
       : "scc");
 }
 
+// Issue priority v (0, 1 or 2), the same way.
+__device__ __forceinline__ void set_priority_0_to_2(uint32_t v) {
+  asm volatile(
+      "s_cmp_eq_u32 %0, 0\n\t"
+      "s_cbranch_scc0 1f\n\t"
+      "s_setprio 0\n\t"
+      "s_branch 3f\n"
+      "1:\n\t"
+      "s_cmp_eq_u32 %0, 1\n\t"
+      "s_cbranch_scc0 2f\n\t"
+      "s_setprio 1\n\t"
+      "s_branch 3f\n"
+      "2:\n\t"
+      "s_setprio 2\n"
+      "3:"
+      :
+      : "s"(v)
+      : "scc");
+}
+
 // fp6 operand (32 codes, six words) of the two packed units in words 4h .. 4h+3 of w: unit
 // words (w0, w1) -> fields T0 = w0 & ~kFp6Exp0, T1 = w1 & ~kFp6Exp1,
 // T2 = (w0 & kFp6Exp0) | (w1 & kFp6Exp1).  The last two words are not read by the fp6 MFMA.
@@ -485,7 +505,10 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
     }
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kInFlight));   // own copy of stage s+2 landed, reads done
     ring_barrier();
-    if constexpr (kFair) set_priority_from_bit0((tnow >> kFairBit) ^ fair_parity);
+    // the second workgroup on the compute unit takes 2 on its turn and 1 off it, the first 1 and
+    // 0: where their clock reads straddle a turn, the second wins the tie the older would win
+    // (event-timed 2048 x 11008 x 4096, four alternating pairs: 83.4-83.9 -> 82.9-83.3 us)
+    if constexpr (kFair) set_priority_0_to_2((((tnow >> kFairBit) ^ fair_parity) & 1u) + fair_parity);
     apply(T::kTM - 1, 1, acc1, sp1, s);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
