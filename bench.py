@@ -575,9 +575,11 @@ def main():
         if all(v is not None for v in vals):
             traffic = float(np.mean(vals))
 
+    where = ("at Llama-7B shapes" if set(keys) <= {"A", "B", "C"} else
+             "at the Llama-70B MLP shape" if keys == ["D"] else
+             "at 16-token batches through the Llama-7B weight shapes")
     line = {
-        "metric": ("effective W4A8 TOPS (quant+GEMM) at Llama-7B shapes; % of INT8 MFMA peak" if w4a8 else
-                   "effective W4A4 TOPS (quant+GEMM) at Llama-7B shapes; % of INT8 MFMA peak"),
+        "metric": f"effective {'W4A8' if w4a8 else 'W4A4'} TOPS (quant+GEMM) {where}; % of INT8 MFMA peak",
         "value": round(value, 2),
         "unit": "TOP/s",
         "n_gpus": 1,
