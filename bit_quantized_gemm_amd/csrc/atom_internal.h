@@ -44,6 +44,10 @@ struct GemmPlan {
 };
 // Few-rows kernel: at most kSmallMaxM token rows.
 constexpr int kSmallMaxM = 16;
+// Compute units of the device current at the first call (queried once per process; 256 if
+// the query fails).
+int compute_units();
+
 GemmPlan gemm_plan(int M, int N, int K);
 // The same plan for the 128 x 128 tiled kernels only (no few-rows branch).
 GemmPlan gemm_plan_tiled(int M, int N, int K);

@@ -954,7 +954,6 @@ int64_t gemm_workspace_bytes(const GemmPlan& plan) {
   return plan.rem > 0 ? (int64_t)plan.rem * plan.splits * kBM * kBN * (int64_t)sizeof(float) : 0;
 }
 
-namespace {
 // Compute units of the device current at the first call (queried once per process; the
 // initialisation of a function-local static is thread-safe).  256 if the query fails.
 int compute_units() {
@@ -967,7 +966,6 @@ int compute_units() {
   }();
   return cus;
 }
-}  // namespace
 
 hipError_t launch_gemm(const uint8_t* Xq, const uint16_t* sx, const uint8_t* Wq, const uint16_t* sw, int M, int N,
                        int K, uint16_t* Y, float* part, const GemmPlan& plan, hipStream_t stream) {
