@@ -451,8 +451,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
   // Fair turns (kFair: a grid of one round with two workgroups on some compute units).  A SIMD
   // issues the older of two ready waves first, so of two workgroups sharing a compute unit the
   // one dispatched first runs ahead and the other finishes alone.  Workgroups b and
-  // b + fair_cus (the first and second on a compute unit) instead take priority 1 in turns, by a
-  // bit of the real-time clock read at the start of each group and applied after its barrier.
+  // b + fair_cus (the first and second on a compute unit) instead take the higher priority in
+  // turns, by a bit of the real-time clock read at the start of each group and applied after
+  // its barrier.
   const uint32_t fair_parity = kFair ? (blockIdx.x / (unsigned)fair_cus) & 1u : 0u;
   auto int4_group = [&](auto ring, int s) __attribute__((always_inline)) {
     constexpr int p = decltype(ring)::kCur, pn = decltype(ring)::kNext, p2 = decltype(ring)::kAfterNext;
