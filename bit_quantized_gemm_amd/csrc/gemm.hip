@@ -825,7 +825,9 @@ __global__ __launch_bounds__(kBM * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int r0 = (int)min((long long)b * rows_per_wg, (long long)M), r1 = min(r0 + rows_per_wg, M);
   if (r0 < r1) {
     rowq::RowQuant<CHUNKS, PASSES, kRowW4A4> rq(X, perm, M, K, Xq, sx, qlds);
+    rq.load_perm();
     rq.prefetch(r0);
+    rq.finish_offsets();
     for (int r = r0; r < r1; ++r) {
       __syncthreads();                               // everyone finished reading the previous row
       rq.stage();

@@ -100,7 +100,9 @@ __global__ __launch_bounds__(kThreads) void row_quantize_kernel(const uint16_t* 
     }
     return ((int)blockIdx.x + k * (int)gridDim.x) / split;
   };
-  if (valid(0)) rq.prefetch(row_of(0));
+  rq.load_perm();
+  rq.prefetch(valid(0) ? row_of(0) : 0);            // unconditional (see RowQuant::prefetch)
+  rq.finish_offsets();
   for (int k = 0; valid(k); ++k) {
     const int row = row_of(k);
     const int part = blocked ? 0 : ((int)blockIdx.x + k * (int)gridDim.x) - row * split;

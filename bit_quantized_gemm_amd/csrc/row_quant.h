@@ -81,8 +81,10 @@ constexpr int kPassElems = kThreads * kPerThread;    // 4096 reordered elements 
 // One workgroup of kThreads threads quantizing whole rows.  CHUNKS: 16-byte row chunks each
 // thread prefetches (K <= CHUNKS * 2048).  PASSES: passes of 4096 reordered elements per row
 // whose gather offsets stay in registers (K <= PASSES * 4096); 0 = read perm from memory on
-// every row.  Use: construct (computes the gather offsets), prefetch(row), then per row:
-// barrier, stage(), barrier, [prefetch(next row)], quantize(row, ...).
+// every row.  Use: construct, load_perm(), prefetch(first row), finish_offsets(), then per row:
+// barrier, stage(), barrier, [prefetch(next row)], quantize(row, ...).  perm's loads go out
+// first and the first row's right behind them, so the offsets are computed while the row is
+// still in flight.
 template <int CHUNKS, int PASSES, int FMT>
 struct RowQuant {
   const uint16_t* __restrict__ X;
@@ -103,37 +105,64 @@ struct RowQuant {
         G(K_ / ATOM_GROUP), klo(K_ - ATOM_OUTLIERS),
         nchunks(K_ / 8),                              // 16-byte chunks per row
         rb(FMT == kRowA8 ? (size_t)K_ : (size_t)((K_ - ATOM_OUTLIERS) / 2 + ATOM_OUTLIERS)),
-        kmax((unsigned)(K_ - 1)) {
+        kmax((unsigned)(K_ - 1)) {}
+
+  // The gather offsets of this thread's passes are kept in registers (PASSES > 0):
+  // load_perm() reads its perm entries into them, finish_offsets() turns those into offsets.
+  __device__ __forceinline__ void load_perm() {
     if (PASSES > 0) {
 #pragma unroll
       for (int ps = 0; ps < (PASSES > 0 ? PASSES : 1); ++ps) {
         const int c = threadIdx.x * kPerThread + ps * kPassElems;
-        if (c < K) gather_offsets(c, offs[ps]);
+        if (c < K) read_perm(c, offs[ps]);
+      }
+    }
+  }
+  __device__ __forceinline__ void finish_offsets() {
+    if (PASSES > 0) {
+#pragma unroll
+      for (int ps = 0; ps < (PASSES > 0 ? PASSES : 1); ++ps) {
+        const int c = threadIdx.x * kPerThread + ps * kPassElems;
+        if (c < K) perm_to_offsets(offs[ps]);
       }
     }
   }
 
-  // LDS byte offsets of this thread's 16 reordered elements (clamped: a bad perm gives
-  // garbage, never an out-of-range read)
-  __device__ __forceinline__ void gather_offsets(int c, int (&off)[kPerThread]) const {
+  // perm entries c .. c+15
+  __device__ __forceinline__ void read_perm(int c, int (&off)[kPerThread]) const {
 #pragma unroll
     for (int v = 0; v < kPerThread / 4; ++v) {
       const int4 p = *reinterpret_cast<const int4*>(perm + c + 4 * v);
-      const unsigned e[4] = {__builtin_elementwise_min((unsigned)p.x, kmax), __builtin_elementwise_min((unsigned)p.y, kmax),
-                             __builtin_elementwise_min((unsigned)p.z, kmax), __builtin_elementwise_min((unsigned)p.w, kmax)};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) off[4 * v + u] = (int)((((e[u] & 15) >> 1) * QP + (e[u] >> 4)) * 4 + (e[u] & 1) * 2);
+      off[4 * v] = p.x;
+      off[4 * v + 1] = p.y;
+      off[4 * v + 2] = p.z;
+      off[4 * v + 3] = p.w;
     }
   }
 
-  // Loads of this thread's chunks of `row` into registers (in flight until stage()).
+  // The 16 perm entries in off -> LDS byte offsets of those elements in the staged row
+  // (clamped: a bad perm gives garbage, never an out-of-range read).
+  __device__ __forceinline__ void perm_to_offsets(int (&off)[kPerThread]) const {
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const unsigned e = __builtin_elementwise_min((unsigned)off[u], kmax);
+      off[u] = (int)((((e & 15) >> 1) * QP + (e >> 4)) * 4 + (e & 1) * 2);
+    }
+  }
+
+  // LDS byte offsets of this thread's 16 reordered elements at position c.
+  __device__ __forceinline__ void gather_offsets(int c, int (&off)[kPerThread]) const {
+    read_perm(c, off);
+    perm_to_offsets(off);
+  }
+
+  // Loads of this thread's chunks of `row` into registers (in flight until stage()).  Every
+  // load is issued (a chunk past the row end reloads the last one, which stage() skips), so the
+  // compiler's wait counts for loads issued before these need not allow for missing ones.
   __device__ __forceinline__ void prefetch(int row) {
     const u32x4* src = reinterpret_cast<const u32x4*>(X + (size_t)row * K);
 #pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      if (c < nchunks) pre[i] = src[c];
-    }
+    for (int i = 0; i < CHUNKS; ++i) pre[i] = src[min((int)threadIdx.x + i * kThreads, nchunks - 1)];
   }
 
   // The prefetched row into LDS, stored by columns (see quantize.hip).  The caller brackets
