@@ -35,9 +35,12 @@ INT8_PEAK_TOPS = 256 * 2.4e9 * 8192 / 1e12      # 5033: 256 CUs x 2.4 GHz x 8192
 # slightly lower and the reported fraction slightly conservative).
 FP6_PEAK_TOPS = 256 * 2.4e9 * 16384 / 1e12      # 10066: dense fp6 / fp4 MFMA
 HBM_PEAK_GBS = 8000.0
-# the W4A4 GEMM kernels' sources: the kernel file and the LDS stage-ring helpers it includes
-GEMM_SRC = [os.path.join(ROOT, "bit_quantized_gemm_amd", "csrc", f) for f in ("gemm.hip", "lds_ring.h")]
-QUANT_SRC = os.path.join(ROOT, "bit_quantized_gemm_amd", "csrc", "quantize.hip")
+# the sources of the W4A4 GEMM kernels and of the row quantize: each kernel file with every
+# header of this repository that it includes
+_CSRC = os.path.join(ROOT, "bit_quantized_gemm_amd", "csrc")
+_ABI_H = os.path.join(ROOT, "include", "atom.h")
+GEMM_SRC = [os.path.join(_CSRC, f) for f in ("gemm.hip", "lds_ring.h", "row_quant.h", "atom_internal.h")] + [_ABI_H]
+QUANT_SRC = [os.path.join(_CSRC, f) for f in ("quantize.hip", "row_quant.h", "atom_internal.h")] + [_ABI_H]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
 
 WORKLOAD_SETS = {
