@@ -331,3 +331,33 @@ def test_static_scratch_covers_every_split_plan(lib):
             worst = max(worst, bq.atom_gemm_workspace_bytes(M, N, bq.MAX_K))
     assert 0 < worst <= cap
     assert bq.atom_gemm_workspace_bytes(17, 8000, bq.MAX_K) == 315 * 128 * 128 * 4 == worst
+
+
+def _local_includes(path, seen):
+    """Every repository header a source includes, directly or through other headers."""
+    for name in re.findall(r'^#include "([^"]+)"', open(path).read(), re.M):
+        for d in (os.path.join(ROOT, "bit_quantized_gemm_amd", "csrc"), os.path.join(ROOT, "include")):
+            p = os.path.join(d, name)
+            if os.path.exists(p) and p not in seen:
+                seen.add(p)
+                _local_includes(p, seen)
+    return seen
+
+
+def test_bench_traffic_hash_covers_every_included_source():
+    """bench.py reports the committed HBM-traffic counters only while the SHA-256 of the
+    measured kernels' sources is unchanged: that hash must cover each kernel file and every
+    repository header it includes, or a header edit would leave stale counters in the line."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_module", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    csrc = os.path.join(ROOT, "bit_quantized_gemm_amd", "csrc")
+    for main, listed in (("gemm.hip", bench.GEMM_SRC), ("quantize.hip", bench.QUANT_SRC)):
+        want = _local_includes(os.path.join(csrc, main), {os.path.join(csrc, main)})
+        assert set(map(os.path.abspath, listed)) == want, main
+    # the committed counters name the same files, in the order bench.py hashes them
+    import json
+    d = json.load(open(bench.TRAFFIC_FILE))
+    assert [os.path.join(ROOT, f) for f in d["gemm_sources"]] == bench.GEMM_SRC
+    assert [os.path.join(ROOT, f) for f in d["quantize_sources"]] == bench.QUANT_SRC
