@@ -27,11 +27,13 @@
 // and u = fma(e, r, t), the integer nearest clamp(u) (ties to even) equals the clamped integer
 // nearest the correctly rounded fp32 quotient x/s for every fp16 scale s this rule can produce
 // and every fp16 x up to the largest absmax giving that scale (tests/quotient_exhaustive.c
-// walks all 1.8e9 such pairs for both qmax with IEEE fused multiply-adds on the CPU).  The
-// scale itself and r come from a reciprocal and one correction step each, not from an IEEE
-// divide (exact for every fp16 input, see quantize16).  INT8 codes: adding 1.5*2^23 rounds
-// the clamped value to that integer with ties to even and leaves its two's-complement low
-// byte in the low bits of the sum.  INT4 codes: a mixed-precision fma rounds u + 1536 once
+// walks all 1.8e9 such pairs for both qmax with IEEE fused multiply-adds on the CPU).  For a
+// normal scale the clamp never changes that integer (the same walk checks it), so the kernel
+// clamps only in a wave that holds a group with a subnormal scale.  The scale itself and r
+// come from a reciprocal and one correction step each, not from an IEEE divide (exact for
+// every fp16 input, see quantize16).  INT8 codes: adding 1.5*2^23 rounds the (clamped) value
+// to that integer with ties to even and leaves its two's-complement low byte in the low bits
+// of the sum.  INT4 codes: a mixed-precision fma rounds u + 1536 once
 // to fp16 (spacing 1 there), which after subtracting 1536 is the integer code as an fp16
 // value, +0 for a zero code.
 //

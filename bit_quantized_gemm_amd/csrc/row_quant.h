@@ -37,18 +37,22 @@ __device__ __forceinline__ float group_max8(float a) {
   return __builtin_bit_cast(float, u);
 }
 
-// Clamped quotient of x for scale s (> 0) with reciprocal r; its nearest integer (ties to
-// even) is the code.
-__device__ __forceinline__ float code_value(_Float16 xh, float s, float r, float qmax) {
+// Quotient of x for scale s (> 0) with reciprocal r; its nearest integer (ties to even),
+// clamped to [-qmax, qmax], is the code.
+__device__ __forceinline__ float code_quotient(_Float16 xh, float s, float r) {
   const float x = (float)xh;
   // t = x * r, written as an fma with +0 so that it cannot become a plain multiply of a
   // converted x: the two differ only in the sign of a zero product, which then rounds to the
   // same code 0
   const float t = __builtin_fmaf(x, r, 0.0f);
   const float e = __builtin_fmaf(-t, s, x);
-  const float u = __builtin_fmaf(e, r, t);
-  return __builtin_amdgcn_fmed3f(u, -qmax, qmax);
+  return __builtin_fmaf(e, r, t);
 }
+
+// The smallest normal fp16 value.  A normal scale is a / qmax rounded to fp16, within a
+// relative 2^-11 of it, so every quotient of the group lies below qmax + 1/2 and rounds into
+// [-qmax, qmax] by itself; only a subnormal scale (tiny groups) can need the clamp.
+constexpr float kMinNormalHalf = 6.103515625e-05f;
 
 // Adding 1.5 * 2^23 rounds to an integer (ties to even) and leaves it in the low bits.
 constexpr float kRound = 12582912.0f;
@@ -215,7 +219,12 @@ struct RowQuant {
       const float r = s > 0.0f ? __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0) : 0.0f;
       float v[kPerThread];
   #pragma unroll
-      for (int i = 0; i < kPerThread; ++i) v[i] = code_value(x[i], s, r, qmax);
+      for (int i = 0; i < kPerThread; ++i) v[i] = code_quotient(x[i], s, r);
+      // the clamp, only where a group of the wave has a subnormal scale (a uniform branch)
+      if (__builtin_amdgcn_ballot_w64(s > 0.0f && s < kMinNormalHalf) != 0) {
+  #pragma unroll
+        for (int i = 0; i < kPerThread; ++i) v[i] = __builtin_amdgcn_fmed3f(v[i], -qmax, qmax);
+      }
       if (!tail && FMT == kRowW4A8) {
         // offset-binary nibbles: adding 1.5 * 2^23 + 8 leaves code + 8 (1 .. 15) in the low
         // byte; block k (codes 8k .. 8k+7) is the word whose byte j holds codes 8k+j and 8k+j+4

@@ -17,9 +17,11 @@
  * with
  *     clamp(rint(fl32(x / s))) (the definition, IEEE division).
  * A zero scale gives r = 0, so t = 0, e = x, u = 0, and the definition gives code 0.
+ * For a normal scale (s >= 2^-14) it also checks that rint(u) alone, without the clamp, is
+ * the same code: the kernel clamps only where a subnormal scale occurs.
  * Every operation is IEEE binary32 with round to nearest even: fmaf is glibc's correctly
  * rounded fused multiply-add, and the build turns off contraction.
- * Output: "pairs <n> mismatches <m>" and the first few mismatches.
+ * Output: "pairs <n> mismatches <m> unclamped_mismatches <u>" and the first few mismatches.
  */
 #include <math.h>
 #include <stdint.h>
@@ -62,9 +64,9 @@ int main(void) {
   static float xs[0x7C00];
   for (int i = 0; i < 0x7C00; ++i) xs[i] = half_bits_to_float((uint16_t)i);
 
-  long long total = 0, bad = 0;
+  long long total = 0, bad = 0, bad_nc = 0;
   int shown = 0;
-#pragma omp parallel for schedule(dynamic, 64) reduction(+ : total, bad)
+#pragma omp parallel for schedule(dynamic, 64) reduction(+ : total, bad, bad_nc)
   for (int p = 0; p < count; ++p) {
     const float s = half_bits_to_float(pairs[2 * p]);
     const float amax = half_bits_to_float(pairs[2 * p + 1]);
@@ -78,6 +80,16 @@ int main(void) {
         const float code = nearbyintf(clampf(u, qmax));
         const float want = s > 0.0f ? clampf(nearbyintf(x / s), qmax) : 0.0f;
         ++total;
+        if (s >= 0x1p-14f && nearbyintf(u) != code) {
+          ++bad_nc;
+#pragma omp critical
+          {
+            if (shown < 8) {
+              fprintf(stdout, "unclamped mismatch s=%a x=%a u=%a code=%g\n", s, x, u, code);
+              ++shown;
+            }
+          }
+        }
         if (code != want) {
           ++bad;
 #pragma omp critical
@@ -91,7 +103,7 @@ int main(void) {
       }
     }
   }
-  printf("pairs %lld mismatches %lld\n", total, bad);
+  printf("pairs %lld mismatches %lld unclamped_mismatches %lld\n", total, bad, bad_nc);
   free(pairs);
-  return bad ? 1 : 0;
+  return (bad || bad_nc) ? 1 : 0;
 }

@@ -115,7 +115,8 @@ def test_code_quotient_exhaustive(qmax, tmp_path):
     """rint(clamp(u)) with u = fma(fma(-t, s, x), r, t), t = fl32(x * r), r = fl32(1/s), equals
     clamp(rint(fl32(x / s))) for every reachable fp16 scale s and every fp16 x with |x| at most
     the largest absmax that produces s: about 0.9 * 10^9 pairs per qmax, checked by a C program with
-    IEEE binary32 fused multiply-adds (tests/quotient_exhaustive.c)."""
+    IEEE binary32 fused multiply-adds (tests/quotient_exhaustive.c).  For every normal scale the
+    same walk checks that rint(u) needs no clamp (the kernel clamps only for subnormal scales)."""
     import shutil
     import subprocess
 
@@ -137,4 +138,4 @@ def test_code_quotient_exhaustive(qmax, tmp_path):
     # the whole domain was walked: x = +-0 .. +-absmax for every scale (positive fp16 bit
     # patterns are ordered like their values)
     assert n == 2 * int((pairs[:, 1].astype(np.int64) + 1).sum()), out
-    assert "mismatches 0" in out, out
+    assert " mismatches 0 " in out and "unclamped_mismatches 0" in out, out
