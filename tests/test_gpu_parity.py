@@ -263,6 +263,55 @@ def test_gemm_llama70b_sampled():
     np.testing.assert_array_equal(acc, O.group_acc(qxa, qwa))
 
 
+def _exact_operands(M, N, K, seed):
+    """Oracle-packed operands on which every step of the production GEMM is exact: codes in
+    [-1, 1] (INT4 groups) and [-3, 3] (INT8 group), scales 2^-1 or 2^-2 by group and row.  Each
+    term acc_g * sx * sw is then a multiple of 2^-4, every fp32 partial sum is exact, and Y is
+    exactly representable in fp16 while |Y| < 64 (about 6 standard deviations here), so the
+    kernel's Y must equal the oracle's bit for bit and a single accumulator off by one shows."""
+    rng = np.random.default_rng(seed)
+    klo, G = K - O.OUTLIERS, K // O.GROUP
+    qx = rng.integers(-1, 2, size=(M, K), dtype=np.int8)
+    qw = rng.integers(-1, 2, size=(N, K), dtype=np.int8)
+    qx[:, klo:] = rng.integers(-3, 4, size=(M, O.OUTLIERS), dtype=np.int8)
+    qw[:, klo:] = rng.integers(-3, 4, size=(N, O.OUTLIERS), dtype=np.int8)
+    sx = np.where(rng.integers(0, 2, size=(G, M)) == 0, 0.5, 0.25).astype(np.float16)
+    sw = np.where(rng.integers(0, 2, size=(G, N)) == 0, 0.5, 0.25).astype(np.float16)
+    y64 = O.gemm_ref(qx, sx, qw, sw)
+    inside = np.abs(y64) < 64
+    assert inside.mean() > 0.999, "the exact window must hold nearly every output"
+    return qx, sx, qw, sw, O.to_fp16(y64)
+
+
+@pytest.mark.parametrize("key", ["A", "B", "C"])
+def test_gemm_exact_y_llama_shapes(key):
+    """The production GEMM of each Llama-7B shape (A: 64 x 64 tiles in two K parts; B: 688
+    tiles of 128 x 128 over several rounds, later ones at priority 1; C: one round with fair
+    turns), on operands where every fp32 step is exact: Y bit-identical to the oracle's, so the
+    per-group integer sums inside the kernel that atom_gemm runs are exact at full size."""
+    w = synth.get(key)
+    _say(f"[exact Y] {key} {w.M}x{w.N}x{w.K}")
+    qx, sx, qw, sw, y16 = _exact_operands(w.M, w.N, w.K, seed=11 + w.M)
+    Y = host(bq.atom_gemm(dev(O.pack_rows(qx)), dev(sx), dev(O.pack_rows(qw)), dev(sw), w.K))
+    np.testing.assert_array_equal(Y.view(np.uint16), y16.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 4096, 11008), (16, 11008, 4096)])
+def test_gemm_exact_y_split_and_few_rows(M, N, K):
+    """The same exactness through split-K (atom_gemm and atom_gemm_ws) and the few-rows kernel
+    (M <= 16) at Llama widths."""
+    _say(f"[exact Y] M={M} N={N} K={K}")
+    qx, sx, qw, sw, y16 = _exact_operands(M, N, K, seed=M + N + K)
+    args = (dev(O.pack_rows(qx)), dev(sx), dev(O.pack_rows(qw)), dev(sw), K)
+    need = bq.atom_gemm_workspace_bytes(M, N, K)
+    outs = [host(bq.atom_gemm(*args))]
+    if need:
+        ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
+        outs.append(host(bq.atom_gemm_ws(*args, ws)))
+    for Y in outs:
+        np.testing.assert_array_equal(Y.view(np.uint16), y16.view(np.uint16))
+
+
 # --------------------------------------------------------------------------- ragged / edge shapes
 RAGGED = [(1, 1, 256), (2, 3, 256), (37, 200, 384), (130, 129, 1152), (257, 513, 640), (16, 512, 1024),
           (128, 128, 256), (129, 255, 2048), (33, 70, 12416), (20, 48, 16384), (9, 40, 20480),
