@@ -115,6 +115,29 @@ def test_w4a8_gemm_full_output(key):
     assert_y_close(Y, O.gemm_ref(qx, sxr, qw, swr), f"W4A8 {key}")
 
 
+@pytest.mark.parametrize("key", ["A", "B", "C"])
+def test_w4a8_exact_y_llama_shapes(key):
+    """The W4A8 GEMM at the Llama-7B shapes (register-staged tiles on A and B, the LDS-DMA ring
+    on C's long K) on oracle-packed operands where every fp32 step is exact: activation and
+    INT4 weight codes in [-1, 1], INT8 weight codes in [-3, 3], scales 2^-1 or 2^-2.  Every term
+    is a multiple of 2^-4 and |Y| < 64 is exact in fp16, so Y must equal the oracle's bit for
+    bit and a single per-group sum off by one (the offset-binary correction included) shows."""
+    w = synth.get(key)
+    M, N, K = w.M, w.N, w.K
+    _say(f"[w4a8 exact Y] {key} {M}x{N}x{K}")
+    rng = np.random.default_rng(23 + M)
+    klo, G = K - O.OUTLIERS, K // O.GROUP
+    qx = rng.integers(-1, 2, size=(M, K), dtype=np.int8)
+    qw = rng.integers(-1, 2, size=(N, K), dtype=np.int8)
+    qw[:, klo:] = rng.integers(-3, 4, size=(N, O.OUTLIERS), dtype=np.int8)
+    sx = np.where(rng.integers(0, 2, size=(G, M)) == 0, 0.5, 0.25).astype(np.float16)
+    sw = np.where(rng.integers(0, 2, size=(G, N)) == 0, 0.5, 0.25).astype(np.float16)
+    y64 = O.gemm_ref(qx, sx, qw, sw)
+    assert (np.abs(y64) < 64).mean() > 0.999, "the exact window must hold nearly every output"
+    Y = host(bq.atom_gemm_w4a8(dev(O.pack_rows_a8(qx)), dev(sx), dev(O.pack_rows_w4a8(qw)), dev(sw), K))
+    np.testing.assert_array_equal(Y.view(np.uint16), O.to_fp16(y64).view(np.uint16))
+
+
 RAGGED = [(1, 1, 256), (3, 70, 256), (129, 255, 2048), (200, 300, 640), (33, 70, 12416), (9, 40, 32768),
           (33, 70, bq.MAX_K)]
 
