@@ -175,8 +175,9 @@ int atom_gemm_noalloc(const void *Xq, const void *sx, const void *Wq, const void
 /*
  * Per-group integer accumulators (verification aid): acc[g, m, n] = acc_g[m,n] as defined
  * for atom_gemm, computed by the main loop of the kernel atom_gemm runs for this shape (the
- * few-rows kernel for M <= 16, the tiled kernel otherwise).  acc is int32 [G, M, N] (output,
- * G*M*N*4 bytes).
+ * few-rows kernel for M <= 16, the tiled kernel otherwise; where atom_gemm splits the groups
+ * of a 64 x 64 tile between two K parts, the same tiles without the split).  acc is int32
+ * [G, M, N] (output, G*M*N*4 bytes).
  */
 int atom_gemm_group_acc(const void *Xq, const void *Wq, int32_t M, int32_t N, int32_t K,
                         int32_t *acc, void *stream);
