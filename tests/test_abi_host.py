@@ -7,6 +7,7 @@ invalid argument on the host before it touches the HIP runtime.  The calls below
 import ctypes
 import os
 import re
+import sys
 
 import pytest
 
@@ -361,3 +362,14 @@ def test_bench_traffic_hash_covers_every_included_source():
     d = json.load(open(bench.TRAFFIC_FILE))
     assert [os.path.join(ROOT, f) for f in d["gemm_sources"]] == bench.GEMM_SRC
     assert [os.path.join(ROOT, f) for f in d["quantize_sources"]] == bench.QUANT_SRC
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it exits with status 2 and says why, before it
+    imports torch or touches a device."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
