@@ -373,6 +373,9 @@ def main():
     ap.add_argument("--path", default="separate", choices=["separate", "fused"],
                     help="separate: atom_quantize_act then atom_gemm_ws; fused: atom_linear (one persistent "
                          "launch where the shape allows)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time whole steps replayed from HIP graphs (one captured per resident input copy) "
+                         "instead of launching each call from Python")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (steps times), to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -442,7 +445,7 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, evs=None):
+    def step(i, evs=None, stream=stream):
         for si, s in enumerate(sets):
             c = s["copies"][i % R]
             w = s["w"]
@@ -473,13 +476,34 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # --graph: one HIP graph per resident input copy, each holding one whole step (captured on
+    # torch's capture stream after the eager warmup, outside the timed region), then replayed
+    graphs = None
+    if args.graph:
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r, stream=torch.cuda.current_stream(dev))
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+
+    def timed_step(i):
+        if graphs is not None:
+            graphs[i % R].replay()
+        else:
+            step(i)
+
     # ---------------------------------------------------------------- timed region: whole steps
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(i)
+        timed_step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
@@ -604,7 +628,8 @@ def main():
             "activations": "INT8 in every group" if w4a8 else "INT4 + INT8 outlier group",
             "rotating_input_copies": R,
             "path": ("atom_linear: quantize and GEMM in one launch where the shape allows" if fused else
-                     "atom_quantize_act then atom_gemm_ws"),
+                     "atom_quantize_act then atom_gemm_ws")
+                    + ("; timed steps replayed from HIP graphs, one per input copy" if args.graph else ""),
         },
         "roofline": {
             # every W4A8 group runs on the int8 matrix cores
