@@ -509,11 +509,13 @@ def test_gemm_small_m_matches_oracle(M, N, K):
 # --------------------------------------------------------------------------- HIP graph capture
 def test_graph_capture_replays_match_eager():
     """The library allocates and synchronizes nothing, so quantize + GEMM can be captured in a
-    HIP graph.  Four shapes cover the four GEMM paths (whole 64 x 64 tiles, split-K with its
-    finalize kernel, whole 128 x 128 tiles, few rows); the graph is replayed several times with
-    unrelated eager work and new inputs in between, and every replay must equal the eager
-    result bit for bit."""
-    cases = [(256, 4096, 4096), (64, 2048, 4096), (1024, 2048, 1024), (16, 2000, 11008)]
+    HIP graph.  Six shapes cover the GEMM paths (64 x 64 tiles in K parts, split-K with its
+    finalize kernel, whole 128 x 128 tiles in one partial round, in one full round with fair turns
+    (512 tiles) and over several rounds with later ones at priority 1 (567 tiles), few rows); the
+    graph is replayed several times with unrelated eager work and new inputs in between, and
+    every replay must equal the eager result bit for bit."""
+    cases = [(256, 4096, 4096), (64, 2048, 4096), (1024, 2048, 1024), (2048, 4096, 512), (1100, 8000, 384),
+             (16, 2000, 11008)]
     st = torch.cuda.Stream()
     bufs = []
     for i, (M, N, K) in enumerate(cases):
