@@ -407,6 +407,8 @@ def main():
     keys = WORKLOAD_SETS[args.workload]
     R = max(1, args.rotate)
     if args.workload == "Dq":
+        if args.graph:
+            log("--graph applies to the quantize + GEMM workloads; Dq launches each quantize from Python")
         return quant_only(args, torch, bq, synth, dev, R)
 
     # ---------------------------------------------------------------- offline: inputs, perm, weight pack
